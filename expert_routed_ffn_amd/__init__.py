@@ -1,0 +1,284 @@
+"""Python binding of libbeam_moe.so: one Beam-style MoE layer forward on
+MI355X (gfx950).
+
+The functions below carry the C entry points' names and do argument
+marshalling only: they check that the torch tensors are contiguous device
+tensors of the expected dtype and shape, then pass their data pointers and
+the current HIP stream to the library.  Every step of the layer runs in the
+library's HIP kernels; there is no fallback of any kind.  If the library is
+missing, importing this package still works but every call raises.
+
+Layer (TokenSpeed x Reflection Beam blog, "Architecture"; vLLM Beam summary,
+MoE and residual section):
+    route -> permute -> experts -> combine_norm
+"""
+
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbeam_moe.so")
+
+BEAM_F32, BEAM_BF16, BEAM_FP8_E4M3 = 0, 1, 2
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape or dtype",
+          3: "workspace missing or too small", 4: "HIP launch failed"}
+
+SYMBOLS = ("beam_moe_route", "beam_moe_permute", "beam_moe_experts", "beam_moe_combine_norm",
+           "beam_moe_workspace_bytes", "beam_moe_status_string")
+
+
+class BeamMoeCfg(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("n_groups", ctypes.c_int32), ("topk_groups", ctypes.c_int32),
+                ("topk", ctypes.c_int32), ("group_topn", ctypes.c_int32),
+                ("d_ff", ctypes.c_int32), ("routed_scale", ctypes.c_float),
+                ("rms_eps", ctypes.c_float)]
+
+
+@dataclasses.dataclass(frozen=True)
+class LayerCfg:
+    """Shape of one MoE layer.  Beam defaults."""
+    hidden: int = 5120
+    n_experts: int = 256
+    n_groups: int = 8
+    topk_groups: int = 4
+    topk: int = 8
+    group_topn: int = 2
+    d_ff: int = 2560
+    routed_scale: float = 2.5
+    rms_eps: float = 1e-6
+
+    def c(self) -> BeamMoeCfg:
+        return BeamMoeCfg(self.hidden, self.n_experts, self.n_groups, self.topk_groups, self.topk,
+                          self.group_topn, self.d_ff, self.routed_scale, self.rms_eps)
+
+
+class BeamError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loads it on first use; raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                           "(python -c 'import __graft_entry__ as g; g.build()')")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    cfgp = ctypes.POINTER(BeamMoeCfg)
+    L.beam_moe_route.argtypes = [cfgp, i32, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.beam_moe_permute.argtypes = [cfgp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
+    L.beam_moe_experts.argtypes = [cfgp, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32,
+                                   vp, sz, vp, vp]
+    L.beam_moe_combine_norm.argtypes = [cfgp, i32, vp, i32, vp, vp, vp, vp, i32, vp, vp, i32, vp, vp]
+    L.beam_moe_workspace_bytes.argtypes = [cfgp, i32, i32]
+    L.beam_moe_workspace_bytes.restype = sz
+    L.beam_moe_status_string.argtypes = [i32]
+    L.beam_moe_status_string.restype = ctypes.c_char_p
+    for f in ("beam_moe_route", "beam_moe_permute", "beam_moe_experts", "beam_moe_combine_norm"):
+        getattr(L, f).restype = i32
+    _lib = L
+    return L
+
+
+# ------------------------------------------------------------------ helpers
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return BEAM_F32
+    if t.dtype == torch.bfloat16:
+        return BEAM_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return BEAM_FP8_E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _p(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch tensor")
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _check(t, shape, dtypes, name):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype} not in {dtypes}")
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ok(fn, status):
+    if status != 0:
+        raise BeamError(fn, status)
+
+
+def workspace_bytes(cfg: LayerCfg, T: int, w_dtype: int) -> int:
+    return int(lib().beam_moe_workspace_bytes(ctypes.byref(cfg.c()), T, w_dtype))
+
+
+def workspace(cfg: LayerCfg, T: int, w_dtype: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(workspace_bytes(cfg, T, w_dtype), 256), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ entry points
+
+def beam_moe_route(cfg: LayerCfg, x, w_router, bias, topk_ids, topk_w, logits_out=None, ws=None,
+                   stream=None):
+    T = x.shape[0]
+    _check(x, (T, cfg.hidden), (torch.bfloat16, torch.float32), "x")
+    _check(w_router, (cfg.n_experts, cfg.hidden), (torch.float32,), "w_router")
+    _check(bias, (cfg.n_experts,), (torch.float32,), "bias")
+    _check(topk_ids, (T, cfg.topk), (torch.int32,), "topk_ids")
+    _check(topk_w, (T, cfg.topk), (torch.float32,), "topk_w")
+    if logits_out is not None:
+        _check(logits_out, (T, cfg.n_experts), (torch.float32,), "logits_out")
+    st = lib().beam_moe_route(ctypes.byref(cfg.c()), T, _p(x), _dt(x), _p(w_router), _p(bias),
+                              _p(topk_ids), _p(topk_w), _p(logits_out), _p(ws),
+                              0 if ws is None else ws.numel(), _stream(stream))
+    _ok("beam_moe_route", st)
+
+
+def beam_moe_permute(cfg: LayerCfg, topk_ids, expert_offsets, row_token, pair_row, x=None,
+                     x_q=None, x_scale=None, ws=None, stream=None):
+    T = topk_ids.shape[0]
+    TK = T * cfg.topk
+    _check(topk_ids, (T, cfg.topk), (torch.int32,), "topk_ids")
+    _check(expert_offsets, (cfg.n_experts + 1,), (torch.int32,), "expert_offsets")
+    _check(row_token, (TK,), (torch.int32,), "row_token")
+    _check(pair_row, (TK,), (torch.int32,), "pair_row")
+    if x_q is not None:
+        _check(x, (T, cfg.hidden), (torch.bfloat16,), "x")
+        _check(x_q, (T, cfg.hidden), (torch.uint8, torch.float8_e4m3fn), "x_q")
+        _check(x_scale, (T,), (torch.float32,), "x_scale")
+    st = lib().beam_moe_permute(ctypes.byref(cfg.c()), T, _p(topk_ids), _p(expert_offsets),
+                                _p(row_token), _p(pair_row), _p(x), BEAM_BF16, _p(x_q),
+                                _p(x_scale), _p(ws), 0 if ws is None else ws.numel(),
+                                _stream(stream))
+    _ok("beam_moe_permute", st)
+
+
+def beam_moe_experts(cfg: LayerCfg, T, x, expert_offsets, row_token, w_gate_up, w_down, y,
+                     x_scale=None, s_gate_up=None, s_down=None, ws=None, stream=None, events=None):
+    """x: [T,H] f32/bf16 activations, or e4m3 codes (uint8) for fp8 weights."""
+    E, H, F, TK = cfg.n_experts, cfg.hidden, cfg.d_ff, T * cfg.topk
+    w_dt = _dt(w_gate_up)
+    _check(x, (T, H), (w_gate_up.dtype,) if w_dt != BEAM_FP8_E4M3 else (torch.uint8, torch.float8_e4m3fn), "x")
+    _check(expert_offsets, (E + 1,), (torch.int32,), "expert_offsets")
+    _check(row_token, (TK,), (torch.int32,), "row_token")
+    _check(w_gate_up, (E, 2 * F, H), (w_gate_up.dtype,), "w_gate_up")
+    _check(w_down, (E, H, F), (w_gate_up.dtype,), "w_down")
+    _check(y, (TK, H), (torch.float32, torch.bfloat16), "y")
+    if w_dt == BEAM_FP8_E4M3:
+        _check(x_scale, (T,), (torch.float32,), "x_scale")
+        _check(s_gate_up, (E, 2 * F), (torch.float32,), "s_gate_up")
+        _check(s_down, (E, H), (torch.float32,), "s_down")
+    ev = None
+    if events is not None:
+        ev = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e) for e in events])
+    st = lib().beam_moe_experts(ctypes.byref(cfg.c()), T, w_dt, _p(x), w_dt, _p(x_scale),
+                                _p(expert_offsets), _p(row_token), _p(w_gate_up), _p(s_gate_up),
+                                _p(w_down), _p(s_down), _p(y), _dt(y), _p(ws),
+                                0 if ws is None else ws.numel(), _stream(stream),
+                                ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None)
+    _ok("beam_moe_experts", st)
+
+
+def beam_moe_combine_norm(cfg: LayerCfg, y, pair_row, topk_w, h, x_next, gamma_post, gamma_pre, n,
+                          moe_out=None, stream=None):
+    T = h.shape[0]
+    H, TK = cfg.hidden, T * cfg.topk
+    _check(y, (TK, H), (torch.float32, torch.bfloat16), "y")
+    _check(pair_row, (TK,), (torch.int32,), "pair_row")
+    _check(topk_w, (T, cfg.topk), (torch.float32,), "topk_w")
+    _check(h, (T, H), (torch.float32, torch.bfloat16), "h")
+    _check(x_next, (T, H), (h.dtype,), "x_next")
+    _check(gamma_post, (H,), (h.dtype,), "gamma_post")
+    _check(gamma_pre, (H,), (h.dtype,), "gamma_pre")
+    if moe_out is not None:
+        _check(moe_out, (T, H), (torch.float32,), "moe_out")
+    st = lib().beam_moe_combine_norm(ctypes.byref(cfg.c()), T, _p(y), _dt(y), _p(pair_row),
+                                     _p(topk_w), _p(h), _p(x_next), _dt(h), _p(gamma_post),
+                                     _p(gamma_pre), int(n), _p(moe_out), _stream(stream))
+    _ok("beam_moe_combine_norm", st)
+
+
+# ------------------------------------------------------------------ whole layer
+
+@dataclasses.dataclass
+class LayerBuffers:
+    """Device outputs and scratch of one layer call for T tokens."""
+    topk_ids: torch.Tensor
+    topk_w: torch.Tensor
+    logits: torch.Tensor | None
+    expert_offsets: torch.Tensor
+    row_token: torch.Tensor
+    pair_row: torch.Tensor
+    x_q: torch.Tensor | None
+    x_scale: torch.Tensor | None
+    y: torch.Tensor
+    x_next: torch.Tensor
+    moe_out: torch.Tensor | None
+    ws: torch.Tensor
+
+
+def alloc_buffers(cfg: LayerCfg, T: int, act_dtype, w_dtype: int, y_dtype=torch.float32,
+                  keep_logits=False, keep_moe_out=False, device="cuda") -> LayerBuffers:
+    TK = T * cfg.topk
+    d = dict(device=device)
+    fp8 = w_dtype == BEAM_FP8_E4M3
+    return LayerBuffers(
+        topk_ids=torch.empty((T, cfg.topk), dtype=torch.int32, **d),
+        topk_w=torch.empty((T, cfg.topk), dtype=torch.float32, **d),
+        logits=torch.empty((T, cfg.n_experts), dtype=torch.float32, **d) if keep_logits else None,
+        expert_offsets=torch.empty((cfg.n_experts + 1,), dtype=torch.int32, **d),
+        row_token=torch.empty((TK,), dtype=torch.int32, **d),
+        pair_row=torch.empty((TK,), dtype=torch.int32, **d),
+        x_q=torch.empty((T, cfg.hidden), dtype=torch.uint8, **d) if fp8 else None,
+        x_scale=torch.empty((T,), dtype=torch.float32, **d) if fp8 else None,
+        y=torch.empty((TK, cfg.hidden), dtype=y_dtype, **d),
+        x_next=torch.empty((T, cfg.hidden), dtype=act_dtype, **d),
+        moe_out=torch.empty((T, cfg.hidden), dtype=torch.float32, **d) if keep_moe_out else None,
+        ws=workspace(cfg, T, w_dtype, device),
+    )
+
+
+def moe_layer(cfg: LayerCfg, x, w_router, bias, w_gate_up, w_down, h, gamma_post, gamma_pre, n,
+              bufs: LayerBuffers, s_gate_up=None, s_down=None, stream=None, events=None):
+    """Runs the four entry points in order on one stream.  h is updated in
+    place; the other results land in `bufs`."""
+    T = x.shape[0]
+    fp8 = _dt(w_gate_up) == BEAM_FP8_E4M3
+    beam_moe_route(cfg, x, w_router, bias, bufs.topk_ids, bufs.topk_w, bufs.logits, bufs.ws, stream)
+    beam_moe_permute(cfg, bufs.topk_ids, bufs.expert_offsets, bufs.row_token, bufs.pair_row,
+                     x=x if fp8 else None, x_q=bufs.x_q, x_scale=bufs.x_scale, ws=bufs.ws,
+                     stream=stream)
+    beam_moe_experts(cfg, T, bufs.x_q if fp8 else x, bufs.expert_offsets, bufs.row_token,
+                     w_gate_up, w_down, bufs.y, x_scale=bufs.x_scale, s_gate_up=s_gate_up,
+                     s_down=s_down, ws=bufs.ws, stream=stream, events=events)
+    beam_moe_combine_norm(cfg, bufs.y, bufs.pair_row, bufs.topk_w, h, bufs.x_next, gamma_post,
+                          gamma_pre, n, bufs.moe_out, stream)

@@ -1,0 +1,227 @@
+// C ABI entry points: argument validation, workspace carving and launches.
+// Every check runs on the host before anything is enqueued.
+#include "beam_moe.h"
+
+#include <math.h>
+
+#include "kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxT = 1 << 22;   // T*K stays far below 2^31
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int epl_of(int E) { return beam::route_epl(E); }
+
+beam_status check_cfg(const beam_moe_cfg* c) {
+    if (!c) return BEAM_ERR_INVALID_ARG;
+    if (c->hidden <= 0 || c->n_experts <= 0 || c->n_groups <= 0 || c->topk_groups <= 0 ||
+        c->topk <= 0 || c->group_topn <= 0 || c->d_ff <= 0)
+        return BEAM_ERR_INVALID_ARG;
+    if (!(c->routed_scale > 0.f) || !isfinite(c->routed_scale) || !(c->rms_eps >= 0.f) ||
+        !isfinite(c->rms_eps))
+        return BEAM_ERR_INVALID_ARG;
+    if (c->hidden % 256 != 0 || c->hidden > 8192) return BEAM_ERR_UNSUPPORTED;
+    if (c->n_experts > 256 || c->n_experts % c->n_groups != 0) return BEAM_ERR_UNSUPPORTED;
+    const int per = c->n_experts / c->n_groups;
+    const int epl = epl_of(c->n_experts);
+    if (per % epl != 0) return BEAM_ERR_UNSUPPORTED;
+    const int lpg = per / epl;
+    if ((lpg & (lpg - 1)) != 0 || lpg * c->n_groups > 64) return BEAM_ERR_UNSUPPORTED;
+    if (c->topk_groups > c->n_groups) return BEAM_ERR_INVALID_ARG;
+    if (c->group_topn > per || c->group_topn > 4) return BEAM_ERR_UNSUPPORTED;
+    if (c->topk > c->topk_groups * per) return BEAM_ERR_INVALID_ARG;
+    if (c->topk > 32) return BEAM_ERR_UNSUPPORTED;
+    if (c->d_ff % 128 != 0 || c->d_ff > 8192) return BEAM_ERR_UNSUPPORTED;
+    return BEAM_OK;
+}
+
+bool valid_dtype(beam_dtype d) { return d == BEAM_F32 || d == BEAM_BF16 || d == BEAM_FP8_E4M3; }
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+size_t route_ws(const beam_moe_cfg* c, int T) { return align256((size_t)T * c->n_experts * sizeof(float)); }
+
+beam::WKind wkind(beam_dtype d) {
+    return d == BEAM_BF16 ? beam::W_BF16 : (d == BEAM_FP8_E4M3 ? beam::W_FP8 : beam::W_F32);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* beam_moe_status_string(beam_status s) {
+    switch (s) {
+        case BEAM_OK: return "ok";
+        case BEAM_ERR_INVALID_ARG: return "invalid argument";
+        case BEAM_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+        case BEAM_ERR_WORKSPACE: return "workspace missing or too small";
+        case BEAM_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+size_t beam_moe_workspace_bytes(const beam_moe_cfg* cfg, int32_t T, beam_dtype w_dtype) {
+    if (check_cfg(cfg) != BEAM_OK || T < 0 || T > kMaxT || !valid_dtype(w_dtype)) return 0;
+    if (T == 0) return 256;
+    size_t b = route_ws(cfg, T);
+    const size_t pb = beam::permute_ws_bytes(T, cfg->topk, cfg->n_experts);
+    const size_t eb = beam::experts_ws_bytes(T, cfg->topk, cfg->n_experts, cfg->hidden, cfg->d_ff,
+                                             wkind(w_dtype));
+    if (pb > b) b = pb;
+    if (eb > b) b = eb;
+    return b;
+}
+
+beam_status beam_moe_route(const beam_moe_cfg* cfg, int32_t T, const void* x, beam_dtype x_dtype,
+                           const float* w_router, const float* bias, int32_t* topk_ids,
+                           float* topk_w, float* logits_out, void* ws, size_t ws_bytes,
+                           void* stream) {
+    beam_status st = check_cfg(cfg);
+    if (st != BEAM_OK) return st;
+    if (T < 0 || T > kMaxT) return BEAM_ERR_INVALID_ARG;
+    if (x_dtype != BEAM_BF16 && x_dtype != BEAM_F32) return BEAM_ERR_INVALID_ARG;
+    if (T == 0) return BEAM_OK;
+    if (!x || !w_router || !bias || !topk_ids || !topk_w) return BEAM_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w_router) || (logits_out && !aligned16(logits_out)))
+        return BEAM_ERR_INVALID_ARG;
+    float* logits = logits_out;
+    if (!logits) {
+        if (!ws || ws_bytes < route_ws(cfg, T)) return BEAM_ERR_WORKSPACE;
+        logits = static_cast<float*>(ws);
+    }
+    beam::RouteArgs a{};
+    a.T = T;
+    a.H = cfg->hidden;
+    a.E = cfg->n_experts;
+    a.G = cfg->n_groups;
+    a.kg = cfg->topk_groups;
+    a.K = cfg->topk;
+    a.topn = cfg->group_topn;
+    a.scale = cfg->routed_scale;
+    a.x = x;
+    a.x_bf16 = x_dtype == BEAM_BF16;
+    a.w = w_router;
+    a.bias = bias;
+    a.logits = logits;
+    a.ids = topk_ids;
+    a.wts = topk_w;
+    return beam::launch_route(a, static_cast<hipStream_t>(stream)) == hipSuccess ? BEAM_OK
+                                                                                  : BEAM_ERR_HIP;
+}
+
+beam_status beam_moe_permute(const beam_moe_cfg* cfg, int32_t T, const int32_t* topk_ids,
+                             int32_t* expert_offsets, int32_t* row_token, int32_t* pair_row,
+                             const void* x, beam_dtype x_dtype, uint8_t* x_q, float* x_scale,
+                             void* ws, size_t ws_bytes, void* stream) {
+    beam_status st = check_cfg(cfg);
+    if (st != BEAM_OK) return st;
+    if (T < 0 || T > kMaxT) return BEAM_ERR_INVALID_ARG;
+    if (T == 0) return BEAM_OK;
+    if (!topk_ids || !expert_offsets || !row_token || !pair_row) return BEAM_ERR_INVALID_ARG;
+    if (x_q) {
+        if (!x || !x_scale || x_dtype != BEAM_BF16) return BEAM_ERR_INVALID_ARG;
+        if (!aligned16(x) || !aligned16(x_q)) return BEAM_ERR_INVALID_ARG;
+    }
+    const size_t need = beam::permute_ws_bytes(T, cfg->topk, cfg->n_experts);
+    if (need > 0 && (!ws || ws_bytes < need)) return BEAM_ERR_WORKSPACE;
+    beam::PermuteArgs a{};
+    a.T = T;
+    a.K = cfg->topk;
+    a.E = cfg->n_experts;
+    a.H = cfg->hidden;
+    a.ids = topk_ids;
+    a.offsets = expert_offsets;
+    a.row_token = row_token;
+    a.pair_row = pair_row;
+    a.x = static_cast<const uint16_t*>(x);
+    a.xq = x_q;
+    a.xscale = x_scale;
+    a.ws = ws;
+    return beam::launch_permute(a, static_cast<hipStream_t>(stream)) == hipSuccess ? BEAM_OK
+                                                                                    : BEAM_ERR_HIP;
+}
+
+beam_status beam_moe_experts(const beam_moe_cfg* cfg, int32_t T, beam_dtype w_dtype, const void* x,
+                             beam_dtype x_dtype, const float* x_scale, const int32_t* expert_offsets,
+                             const int32_t* row_token, const void* w_gate_up, const float* s_gate_up,
+                             const void* w_down, const float* s_down, void* y, beam_dtype y_dtype,
+                             void* ws, size_t ws_bytes, void* stream, void* const* events) {
+    beam_status st = check_cfg(cfg);
+    if (st != BEAM_OK) return st;
+    if (T < 0 || T > kMaxT) return BEAM_ERR_INVALID_ARG;
+    if (!valid_dtype(w_dtype) || !valid_dtype(x_dtype) || !valid_dtype(y_dtype))
+        return BEAM_ERR_INVALID_ARG;
+    if (x_dtype != w_dtype) return BEAM_ERR_INVALID_ARG;
+    if (y_dtype == BEAM_FP8_E4M3) return BEAM_ERR_INVALID_ARG;
+    if (w_dtype == BEAM_FP8_E4M3 && (cfg->hidden % 256 != 0 || cfg->d_ff % 256 != 0))
+        return BEAM_ERR_UNSUPPORTED;
+    if (T == 0) return BEAM_OK;
+    if (!x || !expert_offsets || !row_token || !w_gate_up || !w_down || !y) return BEAM_ERR_INVALID_ARG;
+    if (w_dtype == BEAM_FP8_E4M3 && (!x_scale || !s_gate_up || !s_down)) return BEAM_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(y))
+        return BEAM_ERR_INVALID_ARG;
+    if (w_dtype == BEAM_FP8_E4M3 && (!aligned16(s_gate_up) || !aligned16(s_down)))
+        return BEAM_ERR_INVALID_ARG;
+    const beam::WKind wk = wkind(w_dtype);
+    const size_t need = beam::experts_ws_bytes(T, cfg->topk, cfg->n_experts, cfg->hidden, cfg->d_ff, wk);
+    if (!ws || ws_bytes < need || !aligned16(ws)) return BEAM_ERR_WORKSPACE;
+    beam::ExpertsArgs a{};
+    a.T = T;
+    a.K = cfg->topk;
+    a.E = cfg->n_experts;
+    a.H = cfg->hidden;
+    a.F = cfg->d_ff;
+    a.w = wk;
+    a.x = x;
+    a.xscale = x_scale;
+    a.offsets = expert_offsets;
+    a.row_token = row_token;
+    a.wgu = w_gate_up;
+    a.sgu = s_gate_up;
+    a.wd = w_down;
+    a.sd = s_down;
+    a.y = y;
+    a.y_bf16 = y_dtype == BEAM_BF16;
+    a.ws = ws;
+    for (int i = 0; i < 4; ++i) a.ev[i] = events ? static_cast<hipEvent_t>(events[i]) : nullptr;
+    return beam::launch_experts(a, static_cast<hipStream_t>(stream)) == hipSuccess ? BEAM_OK
+                                                                                    : BEAM_ERR_HIP;
+}
+
+beam_status beam_moe_combine_norm(const beam_moe_cfg* cfg, int32_t T, const void* y,
+                                  beam_dtype y_dtype, const int32_t* pair_row, const float* topk_w,
+                                  void* h, void* x_next, beam_dtype act_dtype, const void* gamma_post,
+                                  const void* gamma_pre, int32_t n, float* moe_out, void* stream) {
+    beam_status st = check_cfg(cfg);
+    if (st != BEAM_OK) return st;
+    if (T < 0 || T > kMaxT || n < 1) return BEAM_ERR_INVALID_ARG;
+    if ((y_dtype != BEAM_F32 && y_dtype != BEAM_BF16) || (act_dtype != BEAM_F32 && act_dtype != BEAM_BF16))
+        return BEAM_ERR_INVALID_ARG;
+    if (T == 0) return BEAM_OK;
+    if (!y || !pair_row || !topk_w || !h || !x_next || !gamma_post || !gamma_pre)
+        return BEAM_ERR_INVALID_ARG;
+    if (h == x_next) return BEAM_ERR_INVALID_ARG;
+    beam::CombineArgs a{};
+    a.T = T;
+    a.K = cfg->topk;
+    a.H = cfg->hidden;
+    a.y = y;
+    a.y_bf16 = y_dtype == BEAM_BF16;
+    a.pair_row = pair_row;
+    a.w = topk_w;
+    a.h = h;
+    a.x_next = x_next;
+    a.act_bf16 = act_dtype == BEAM_BF16;
+    a.gpost = gamma_post;
+    a.gpre = gamma_pre;
+    a.c_res = (float)sqrt((double)(n - 1) / (double)n);
+    a.c_new = (float)(1.0 / sqrt((double)n));
+    a.eps = cfg->rms_eps;
+    a.moe_out = moe_out;
+    return beam::launch_combine_norm(a, static_cast<hipStream_t>(stream)) == hipSuccess ? BEAM_OK
+                                                                                         : BEAM_ERR_HIP;
+}
+
+}  // extern "C"

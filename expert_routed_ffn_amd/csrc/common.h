@@ -1,0 +1,157 @@
+// Device helpers shared by the Beam MoE kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define BEAM_DEV __device__ __forceinline__
+
+namespace beam {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------- bf16 bits
+
+BEAM_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// round-to-nearest-even fp32 -> bf16; NaN stays a (quiet) NaN
+BEAM_DEV uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return uint16_t((u >> 16) | 0x40u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return uint16_t(u >> 16);
+}
+
+// ---------------------------------------------------------------- e4m3 bits
+
+// OCP E4M3FN encode: round to nearest even, saturate to +-448, NaN -> 0x7F.
+BEAM_DEV uint32_t f32_to_e4m3(float f) {
+    uint32_t u = __float_as_uint(f);
+    uint32_t sign = (u >> 24) & 0x80u;
+    uint32_t a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u) return sign | 0x7Fu;          // NaN
+    if (a >= 0x43E00000u) return sign | 0x7Eu;         // |f| >= 448 (incl. inf)
+    if (a < 0x3C800000u) {                             // |f| < 2^-6: step 2^-9
+        float s = __uint_as_float(a) * 512.0f;         // exact, < 8
+        return sign | uint32_t(rintf(s));              // 8 -> 0x08 = 2^-6
+    }
+    uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;   // keep 3 mantissa bits, RNE
+    return sign | (r - (120u << 3));                   // rebias exponent 127 -> 7
+}
+
+// ---------------------------------------------------------------- reductions
+
+BEAM_DEV float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+BEAM_DEV float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+// Block-wide sum; `red` is __shared__ float[blockDim/64]; every thread gets the sum.
+template <int NWAVES>
+BEAM_DEV float block_sum(float v, float* red) {
+    v = wave_sum(v);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 0) red[w] = v;
+    __syncthreads();
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NWAVES; ++i) s += red[i];
+    __syncthreads();
+    return s;
+}
+
+template <int NWAVES>
+BEAM_DEV float block_max(float v, float* red) {
+    v = wave_max(v);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 0) red[w] = v;
+    __syncthreads();
+    float s = red[0];
+#pragma unroll
+    for (int i = 1; i < NWAVES; ++i) s = fmaxf(s, red[i]);
+    __syncthreads();
+    return s;
+}
+
+// order-preserving map of an fp32 onto uint32 (larger float -> larger uint)
+BEAM_DEV uint32_t ordered_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+BEAM_DEV float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+
+}  // namespace beam
+
+namespace beam {
+
+// Dynamic per-row e4m3 quantisation of `n` values read through `load(i)`
+// (n <= 8 * 1024, n % 4 == 0) by one 256-thread workgroup:
+//   scale = amax / 448 (correctly rounded fp32; 1 for an all-zero row),
+//   code  = e4m3(v / scale) with a correctly rounded fp32 division.
+constexpr int kQuantMaxIter = 8;
+template <typename Load4>
+BEAM_DEV void quantize_row_e4m3(Load4 load4, int n, uint8_t* __restrict__ q, float* scale_out,
+                                float* red) {
+    float v[kQuantMaxIter][4];
+    float amax = 0.f;
+#pragma unroll
+    for (int it = 0; it < kQuantMaxIter; ++it) {
+        const int i = (it * 256 + threadIdx.x) * 4;
+        if (i < n) {
+            const float4 f = load4(i);
+            v[it][0] = f.x; v[it][1] = f.y; v[it][2] = f.z; v[it][3] = f.w;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(v[it][j]));
+        }
+    }
+    amax = block_max<4>(amax, red);
+    const float s = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+#pragma unroll
+    for (int it = 0; it < kQuantMaxIter; ++it) {
+        const int i = (it * 256 + threadIdx.x) * 4;
+        if (i < n) {
+            uint32_t c = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) c |= f32_to_e4m3(__fdiv_rn(v[it][j], s)) << (8 * j);
+            *reinterpret_cast<uint32_t*>(q + i) = c;
+        }
+    }
+    if (threadIdx.x == 0) *scale_out = s;
+}
+
+// Exclusive prefix sum of v over a 256-thread block.  Returns the exclusive
+// value; *total gets the block total.  `tmp` is __shared__ int[4].
+BEAM_DEV int block_exclusive_scan(int v, int* tmp, int* total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += u;
+    }
+    if (lane == 63) tmp[w] = incl;
+    __syncthreads();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        before += (i < w) ? tmp[i] : 0;
+        tot += tmp[i];
+    }
+    __syncthreads();
+    *total = tot;
+    return before + incl - v;
+}
+
+}  // namespace beam

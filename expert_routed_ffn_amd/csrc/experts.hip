@@ -1,0 +1,410 @@
+// Grouped SwiGLU experts: GEMM1 (gate and up projections with SwiGLU fused
+// into the epilogue) and GEMM2 (down projection) over the expert-grouped
+// rows, bf16 or fp8-e4m3 on MFMA, plus a plain fp32 path for small shapes.
+// (TokenSpeed x Reflection Beam blog, "TensorRT-LLM NVFP4 MoE": both expert
+//  GEMMs with SwiGLU fused into the first; Gaudi cookbook, "What was built"
+//  and "EP vs TP quality": per-channel FP8 weights, dynamic per-token
+//  activations, down-projection input quantised per token over all d_ff.)
+//
+// Work decomposition.  A work item is (expert e, up to MC consecutive
+// permuted rows of e); items are built on the device from the expert
+// offsets, so the host never reads routing results.  A 256-thread
+// workgroup takes one item and one N-tile of weight rows; each of its 4
+// waves owns two 16-row MFMA tiles of weights (GEMM1: 16 gate rows and the
+// 16 matching up rows, so SwiGLU happens in registers; GEMM2: 32 output
+// rows) and the item's rows in blocks of 16.  Weights stream from HBM
+// straight into MFMA A-operand registers, each weight byte read once per
+// item; activation rows (few, L2-resident) are the B operand.  Per K step a
+// lane loads 64 contiguous bytes of its weight row, so a wave reads 16 rows
+// x 256 contiguous bytes; the MFMA's k index is permuted consistently
+// between A and B to allow that.
+#include "common.h"
+#include "kernels.h"
+
+namespace beam {
+
+constexpr int kKIterBytes = 256;    // bytes of one row consumed per K iteration
+
+BEAM_DEV uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// ---------------------------------------------------------------- items
+
+__global__ __launch_bounds__(256) void beam_build_items(const int32_t* __restrict__ offsets, int E,
+                                                        int MC, int4* __restrict__ items,
+                                                        int* __restrict__ n_items) {
+    __shared__ int tmp[4];
+    const int e = threadIdx.x;
+    const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
+    const int nch = (cnt + MC - 1) / MC;
+    int total;
+    const int first = block_exclusive_scan(nch, tmp, &total);
+    for (int c = 0; c < nch; ++c)
+        items[first + c] = make_int4(e, offsets[e] + c * MC, min(MC, cnt - c * MC), 0);
+    if (e == 0) *n_items = total;
+}
+
+// ---------------------------------------------------------------- MFMA
+
+template <int KIND>
+BEAM_DEV void mfma_kiter(const uint4 (&a)[4], const uint4 (&b)[4], f32x4& acc) {
+    if constexpr (KIND == W_BF16) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[s]),
+                                                          __builtin_bit_cast(bf16x8, b[s]), acc, 0, 0, 0);
+    } else {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const i32x8 av = {(int)a[2 * s].x, (int)a[2 * s].y, (int)a[2 * s].z, (int)a[2 * s].w,
+                              (int)a[2 * s + 1].x, (int)a[2 * s + 1].y, (int)a[2 * s + 1].z,
+                              (int)a[2 * s + 1].w};
+            const i32x8 bv = {(int)b[2 * s].x, (int)b[2 * s].y, (int)b[2 * s].z, (int)b[2 * s].w,
+                              (int)b[2 * s + 1].x, (int)b[2 * s + 1].y, (int)b[2 * s + 1].z,
+                              (int)b[2 * s + 1].w};
+            // formats 0/0 = e4m3 x e4m3; block scales 127 = 2^0 (unscaled)
+            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 0, 0, 0, 127, 0, 127);
+        }
+    }
+}
+
+struct GemmParams {
+    const int4* items;
+    const int* n_items;
+    int n_tiles;
+    const uint8_t* act;        // G1: x rows (bf16 or e4m3), gathered by token; G2: a rows
+    const int32_t* row_token;  // G1 only
+    const float* act_scale;    // fp8: G1 per token, G2 per row
+    const uint8_t* W;          // expert weight stacks
+    const float* wscale;       // fp8: per output row
+    int H, F;
+    void* out;
+    bool out_bf16;             // G2 only
+};
+
+template <int KIND, bool G1, int NB>
+BEAM_DEV void gemm_item(const GemmParams& p, int e, int row0, int rows, int tile) {
+    constexpr int ES = (KIND == W_BF16) ? 2 : 1;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const int kbytes = (G1 ? p.H : p.F) * ES;
+    const int nrows_w = G1 ? 2 * p.F : p.H;
+    const int a0 = G1 ? tile * 64 + wave * 16 : tile * 128 + wave * 32;
+    const int a1 = G1 ? p.F + a0 : a0 + 16;
+    const uint8_t* We = p.W + (size_t)e * nrows_w * kbytes;
+    const uint8_t* pa0 = We + (size_t)(a0 + r) * kbytes + 64 * g;
+    const uint8_t* pa1 = We + (size_t)(a1 + r) * kbytes + 64 * g;
+
+    const uint8_t* pb[NB];
+    bool bval[NB];
+    int tok[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int c = nb * 16 + r;
+        bval[nb] = c < rows;
+        if constexpr (G1) {
+            tok[nb] = bval[nb] ? p.row_token[row0 + c] : 0;
+            pb[nb] = p.act + (size_t)tok[nb] * kbytes + 64 * g;
+        } else {
+            tok[nb] = row0 + c;
+            pb[nb] = p.act + (size_t)(bval[nb] ? row0 + c : row0) * kbytes + 64 * g;
+        }
+    }
+
+    f32x4 acc0[NB], acc1[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        acc0[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc1[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    uint4 wa0[2][4], wa1[2][4], xb[2][NB][4];
+    auto load = [&](int buf, int k) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            wa0[buf][s] = ld16(pa0 + k + 16 * s);
+            wa1[buf][s] = ld16(pa1 + k + 16 * s);
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                xb[buf][nb][s] = bval[nb] ? ld16(pb[nb] + k + 16 * s) : make_uint4(0, 0, 0, 0);
+    };
+    auto compute = [&](int buf) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            mfma_kiter<KIND>(wa0[buf], xb[buf][nb], acc0[nb]);
+            mfma_kiter<KIND>(wa1[buf], xb[buf][nb], acc1[nb]);
+        }
+    };
+
+    load(0, 0);
+    for (int k = 0; k < kbytes; k += 2 * kKIterBytes) {
+        const bool has1 = k + kKIterBytes < kbytes;
+        if (has1) load(1, k + kKIterBytes);
+        compute(0);
+        if (k + 2 * kKIterBytes < kbytes) load(0, k + 2 * kKIterBytes);
+        if (has1) compute(1);
+    }
+
+    // epilogue: lane holds D[4g+i][r] = output row (a0/a1 + 4g + i) x item row (nb*16 + r)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        if (!bval[nb]) continue;
+        const size_t row = (size_t)row0 + nb * 16 + r;
+        if constexpr (G1) {
+            const int f = a0 + 4 * g;
+            float gv[4], uv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { gv[i] = acc0[nb][i]; uv[i] = acc1[nb][i]; }
+            if constexpr (KIND == W_FP8) {
+                const float sx = p.act_scale[tok[nb]];
+                const float4 sg = *reinterpret_cast<const float4*>(p.wscale + (size_t)e * nrows_w + f);
+                const float4 su = *reinterpret_cast<const float4*>(p.wscale + (size_t)e * nrows_w + p.F + f);
+                gv[0] *= sx * sg.x; gv[1] *= sx * sg.y; gv[2] *= sx * sg.z; gv[3] *= sx * sg.w;
+                uv[0] *= sx * su.x; uv[1] *= sx * su.y; uv[2] *= sx * su.z; uv[3] *= sx * su.w;
+                float4 av;
+                av.x = silu_f32(gv[0]) * uv[0];
+                av.y = silu_f32(gv[1]) * uv[1];
+                av.z = silu_f32(gv[2]) * uv[2];
+                av.w = silu_f32(gv[3]) * uv[3];
+                *reinterpret_cast<float4*>(static_cast<float*>(p.out) + row * p.F + f) = av;
+            } else {
+                uint16_t hb[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16(silu_f32(gv[i]) * uv[i]);
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + row * p.F + f) =
+                    make_uint2(hb[0] | (uint32_t(hb[1]) << 16), hb[2] | (uint32_t(hb[3]) << 16));
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int o = (t == 0 ? a0 : a1) + 4 * g;
+                float v[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = (t == 0 ? acc0[nb][i] : acc1[nb][i]);
+                if constexpr (KIND == W_FP8) {
+                    const float sa = p.act_scale[row];
+                    const float4 sw = *reinterpret_cast<const float4*>(p.wscale + (size_t)e * nrows_w + o);
+                    v[0] *= sa * sw.x; v[1] *= sa * sw.y; v[2] *= sa * sw.z; v[3] *= sa * sw.w;
+                }
+                if (p.out_bf16) {
+                    uint16_t hb[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16(v[i]);
+                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + row * p.H + o) =
+                        make_uint2(hb[0] | (uint32_t(hb[1]) << 16), hb[2] | (uint32_t(hb[3]) << 16));
+                } else {
+                    *reinterpret_cast<float4*>(static_cast<float*>(p.out) + row * p.H + o) =
+                        make_float4(v[0], v[1], v[2], v[3]);
+                }
+            }
+        }
+    }
+}
+
+template <int KIND, bool G1, int NBMAX>
+__global__ __launch_bounds__(256) void beam_expert_gemm(GemmParams p) {
+    const int item = blockIdx.x / p.n_tiles;
+    const int tile = blockIdx.x - item * p.n_tiles;
+    if (item >= *p.n_items) return;
+    const int4 it = p.items[item];
+    if constexpr (NBMAX == 1) {
+        gemm_item<KIND, G1, 1>(p, it.x, it.y, it.z, tile);
+    } else {
+        if (it.z <= 16)
+            gemm_item<KIND, G1, 1>(p, it.x, it.y, it.z, tile);
+        else if (it.z <= 32)
+            gemm_item<KIND, G1, 2>(p, it.x, it.y, it.z, tile);
+        else
+            gemm_item<KIND, G1, 4>(p, it.x, it.y, it.z, tile);
+    }
+}
+
+// Per-row e4m3 re-quantisation of the fp32 SwiGLU output (fp8 path).
+__global__ __launch_bounds__(256) void beam_quantize_a_e4m3(const float* __restrict__ a,
+                                                            const int32_t* __restrict__ offsets, int E,
+                                                            int F, uint8_t* __restrict__ aq,
+                                                            float* __restrict__ ascale) {
+    __shared__ float red[4];
+    const size_t row = blockIdx.x;
+    if (row >= (size_t)offsets[E]) return;
+    const float* ar = a + row * F;
+    auto load4 = [&](int i) { return *reinterpret_cast<const float4*>(ar + i); };
+    quantize_row_e4m3(load4, F, aq + row * F, ascale + row, red);
+}
+
+// ---------------------------------------------------------------- fp32 path
+// One workgroup per permuted row; plain fp32 FMA dot products.
+
+BEAM_DEV int expert_of_row(const int32_t* offsets, int E, int row) {
+    int lo = 0, hi = E;   // largest e with offsets[e] <= row
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (offsets[mid] <= row) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+__global__ __launch_bounds__(256) void beam_expert_f32_gemm1(
+    const float* __restrict__ x, const int32_t* __restrict__ offsets, const int32_t* __restrict__ row_token,
+    const float* __restrict__ wgu, int E, int H, int F, float* __restrict__ a) {
+    const int row = blockIdx.x;
+    if (row >= offsets[E]) return;
+    const int e = expert_of_row(offsets, E, row);
+    const float* xr = x + (size_t)row_token[row] * H;
+    for (int j = threadIdx.x; j < F; j += blockDim.x) {
+        const float* wg = wgu + ((size_t)e * 2 * F + j) * H;
+        const float* wu = wgu + ((size_t)e * 2 * F + F + j) * H;
+        float gs = 0.f, us = 0.f;
+        for (int i = 0; i < H; ++i) {
+            gs = fmaf(xr[i], wg[i], gs);
+            us = fmaf(xr[i], wu[i], us);
+        }
+        a[(size_t)row * F + j] = (gs / (1.0f + expf(-gs))) * us;
+    }
+}
+
+__global__ __launch_bounds__(256) void beam_expert_f32_gemm2(
+    const float* __restrict__ a, const int32_t* __restrict__ offsets, const float* __restrict__ wd,
+    int E, int H, int F, void* __restrict__ y, bool y_bf16) {
+    const int row = blockIdx.x;
+    if (row >= offsets[E]) return;
+    const int e = expert_of_row(offsets, E, row);
+    const float* ar = a + (size_t)row * F;
+    for (int o = threadIdx.x; o < H; o += blockDim.x) {
+        const float* w = wd + ((size_t)e * H + o) * F;
+        float s = 0.f;
+        for (int j = 0; j < F; ++j) s = fmaf(ar[j], w[j], s);
+        if (y_bf16)
+            static_cast<uint16_t*>(y)[(size_t)row * H + o] = f32_to_bf16(s);
+        else
+            static_cast<float*>(y)[(size_t)row * H + o] = s;
+    }
+}
+
+// ---------------------------------------------------------------- host side
+
+static size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+static int rows_per_item(int T) { return T <= 16 ? 16 : 64; }
+
+static size_t max_items(int T, int K, int E) {
+    const size_t TK = (size_t)T * K;
+    return TK / rows_per_item(T) + (size_t)std::min<size_t>(E, TK);
+}
+
+struct ExpertsWs {
+    int* n_items;
+    int4* items;
+    void* a;        // bf16 [TK,F] (BF16) or fp32 [TK,F] (FP8, F32)
+    uint8_t* aq;    // FP8: e4m3 [TK,F]
+    float* ascale;  // FP8: [TK]
+    size_t bytes;
+};
+
+static ExpertsWs carve(void* base, int T, int K, int E, int F, WKind w) {
+    const size_t TK = (size_t)T * K;
+    ExpertsWs s{};
+    uint8_t* p = static_cast<uint8_t*>(base);
+    size_t off = 0;
+    s.n_items = reinterpret_cast<int*>(p + off);
+    off += 256;
+    s.items = reinterpret_cast<int4*>(p + off);
+    off += align256(max_items(T, K, E) * sizeof(int4));
+    s.a = p + off;
+    off += align256(TK * F * (w == W_BF16 ? 2 : 4));
+    if (w == W_FP8) {
+        s.aq = p + off;
+        off += align256(TK * F);
+        s.ascale = reinterpret_cast<float*>(p + off);
+        off += align256(TK * sizeof(float));
+    }
+    s.bytes = off;
+    return s;
+}
+
+size_t experts_ws_bytes(int T, int K, int E, int H, int F, WKind w) {
+    (void)H;
+    return carve(nullptr, T, K, E, F, w).bytes;
+}
+
+template <int KIND, bool G1>
+static void launch_gemm(const GemmParams& p, int n_blocks, int nbmax, hipStream_t st) {
+    if (nbmax == 1)
+        hipLaunchKernelGGL((beam_expert_gemm<KIND, G1, 1>), dim3(n_blocks), dim3(256), 0, st, p);
+    else
+        hipLaunchKernelGGL((beam_expert_gemm<KIND, G1, 4>), dim3(n_blocks), dim3(256), 0, st, p);
+}
+
+static void record(hipEvent_t ev, hipStream_t st) {
+    if (ev) (void)hipEventRecord(ev, st);
+}
+
+hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st) {
+    const int TK = a.T * a.K;
+    ExpertsWs ws = carve(a.ws, a.T, a.K, a.E, a.F, a.w);
+    if (a.w == W_F32) {
+        record(a.ev[0], st);
+        hipLaunchKernelGGL(beam_expert_f32_gemm1, dim3(TK), dim3(256), 0, st, (const float*)a.x,
+                           a.offsets, a.row_token, (const float*)a.wgu, a.E, a.H, a.F, (float*)ws.a);
+        record(a.ev[1], st);
+        record(a.ev[2], st);
+        hipLaunchKernelGGL(beam_expert_f32_gemm2, dim3(TK), dim3(256), 0, st, (const float*)ws.a,
+                           a.offsets, (const float*)a.wd, a.E, a.H, a.F, a.y, a.y_bf16);
+        record(a.ev[3], st);
+        return hipGetLastError();
+    }
+    const int mc = rows_per_item(a.T);
+    const int nbmax = mc / 16;
+    const int n_items_max = (int)max_items(a.T, a.K, a.E);
+    hipLaunchKernelGGL(beam_build_items, dim3(1), dim3(256), 0, st, a.offsets, a.E, mc, ws.items,
+                       ws.n_items);
+
+    GemmParams p{};
+    p.items = ws.items;
+    p.n_items = ws.n_items;
+    p.H = a.H;
+    p.F = a.F;
+
+    // GEMM1 + SwiGLU
+    p.n_tiles = a.F / 64;
+    p.act = static_cast<const uint8_t*>(a.x);
+    p.row_token = a.row_token;
+    p.act_scale = a.xscale;
+    p.W = static_cast<const uint8_t*>(a.wgu);
+    p.wscale = a.sgu;
+    p.out = ws.a;
+    p.out_bf16 = false;
+    record(a.ev[0], st);
+    if (a.w == W_BF16)
+        launch_gemm<W_BF16, true>(p, n_items_max * p.n_tiles, nbmax, st);
+    else
+        launch_gemm<W_FP8, true>(p, n_items_max * p.n_tiles, nbmax, st);
+    record(a.ev[1], st);
+
+    // GEMM2
+    p.n_tiles = a.H / 128;
+    p.row_token = nullptr;
+    p.W = static_cast<const uint8_t*>(a.wd);
+    p.wscale = a.sd;
+    p.out = a.y;
+    p.out_bf16 = a.y_bf16;
+    if (a.w == W_FP8) {
+        hipLaunchKernelGGL(beam_quantize_a_e4m3, dim3(TK), dim3(256), 0, st, (const float*)ws.a,
+                           a.offsets, a.E, a.F, ws.aq, ws.ascale);
+        p.act = ws.aq;
+        p.act_scale = ws.ascale;
+        record(a.ev[2], st);
+        launch_gemm<W_FP8, false>(p, n_items_max * p.n_tiles, nbmax, st);
+    } else {
+        p.act = static_cast<const uint8_t*>(ws.a);
+        p.act_scale = nullptr;
+        record(a.ev[2], st);
+        launch_gemm<W_BF16, false>(p, n_items_max * p.n_tiles, nbmax, st);
+    }
+    record(a.ev[3], st);
+    return hipGetLastError();
+}
+
+}  // namespace beam

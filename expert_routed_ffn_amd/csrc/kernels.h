@@ -1,0 +1,76 @@
+// Internal launch interface between the C ABI (beam_moe.hip) and the kernel
+// files.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace beam {
+
+struct RouteArgs {
+    int T, H, E, G, kg, K, topn;
+    float scale;
+    const void* x;
+    bool x_bf16;
+    const float* w;
+    const float* bias;
+    float* logits;      // [T,E] (caller's logits_out or workspace)
+    int32_t* ids;
+    float* wts;
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+int route_epl(int E);
+
+struct PermuteArgs {
+    int T, K, E, H;
+    const int32_t* ids;
+    int32_t* offsets;
+    int32_t* row_token;
+    int32_t* pair_row;
+    const uint16_t* x;  // bf16, only with xq
+    uint8_t* xq;
+    float* xscale;
+    void* ws;
+};
+size_t permute_ws_bytes(int T, int K, int E);
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t st);
+
+enum WKind { W_F32 = 0, W_BF16 = 1, W_FP8 = 2 };
+
+struct ExpertsArgs {
+    int T, K, E, H, F;
+    WKind w;
+    const void* x;          // F32 / BF16 activations or e4m3 codes
+    const float* xscale;    // FP8 only
+    const int32_t* offsets;
+    const int32_t* row_token;
+    const void* wgu;
+    const float* sgu;
+    const void* wd;
+    const float* sd;
+    void* y;
+    bool y_bf16;
+    void* ws;
+    hipEvent_t ev[4];       // optional timing events (null entries skipped)
+};
+size_t experts_ws_bytes(int T, int K, int E, int H, int F, WKind w);
+hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st);
+
+struct CombineArgs {
+    int T, K, H;
+    const void* y;
+    bool y_bf16;
+    const int32_t* pair_row;
+    const float* w;
+    void* h;
+    void* x_next;
+    bool act_bf16;
+    const void* gpost;
+    const void* gpre;
+    float c_res, c_new, eps;
+    float* moe_out;
+};
+hipError_t launch_combine_norm(const CombineArgs& a, hipStream_t st);
+
+}  // namespace beam

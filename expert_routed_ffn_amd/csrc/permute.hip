@@ -1,0 +1,175 @@
+// Permutation: stable expert-major grouping of the T*K (token, slot) pairs
+// via an LDS histogram, an exclusive prefix sum and an order-preserving
+// scatter; plus the optional dynamic per-token e4m3 quantisation of x.
+// (vLLM Beam summary, kernel list: the routing kernels of the MoE path;
+//  TokenSpeed blog, "TensorRT-LLM NVFP4 MoE": input quantisation is
+//  independent of the routes; Gaudi cookbook, "What was built": dynamic
+//  per-token FP8 activations.)
+#include "common.h"
+#include "kernels.h"
+
+namespace beam {
+
+constexpr int kPermThreads = 256;
+constexpr int kPermChunk = 4096;   // pairs per workgroup in the multi-block path
+constexpr int kMaxE = 256;
+
+// Stable scatter of pairs [begin, end) given per-expert cursors in LDS
+// (cursor[e] = first free permuted row of expert e for this range).  Pairs
+// are taken 256 at a time; inside a wave the rank among equal experts comes
+// from ballots over the expert id bits, and the four waves of a chunk
+// claim their rows one after another so the order of p is kept.
+BEAM_DEV void stable_scatter(const int32_t* __restrict__ ids, int begin, int end, int K,
+                             int E, int ebits, int* cursor, int32_t* __restrict__ row_token,
+                             int32_t* __restrict__ pair_row) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int base = begin; base < end; base += kPermThreads) {
+        const int p = base + threadIdx.x;
+        bool valid = p < end;
+        int e = valid ? ids[p] : 0;
+        if ((unsigned)e >= (unsigned)E) { valid = false; e = 0; }   // out-of-range ids are dropped
+        uint64_t peers = __ballot(valid);
+        for (int bit = 0; bit < ebits; ++bit) {
+            const bool b = (e >> bit) & 1;
+            const uint64_t bal = __ballot(valid && b);
+            peers &= b ? bal : ~bal;
+        }
+        const int rank = __popcll(peers & lt_mask);
+        const int cnt = __popcll(peers);
+        for (int ww = 0; ww < kPermThreads / 64; ++ww) {
+            if (w == ww && valid) {
+                const int r = cursor[e] + rank;
+                row_token[r] = p / K;
+                pair_row[p] = r;
+                if (rank == cnt - 1) cursor[e] = r + 1;
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// Whole permutation in one workgroup (T*K <= kPermChunk).
+__global__ __launch_bounds__(kPermThreads) void beam_permute_fused(
+    const int32_t* __restrict__ ids, int TK, int K, int E, int ebits,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ row_token, int32_t* __restrict__ pair_row) {
+    __shared__ int hist[kMaxE];
+    __shared__ int cursor[kMaxE];
+    __shared__ int tmp[4];
+    const int tid = threadIdx.x;
+    if (tid < E) hist[tid] = 0;
+    __syncthreads();
+    for (int p = tid; p < TK; p += kPermThreads) {
+        const int e = ids[p];
+        if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);
+    }
+    __syncthreads();
+    int total;
+    const int excl = block_exclusive_scan(tid < E ? hist[tid] : 0, tmp, &total);
+    if (tid < E) {
+        offsets[tid] = excl;
+        cursor[tid] = excl;
+    }
+    if (tid == 0) offsets[E] = total;
+    __syncthreads();
+    stable_scatter(ids, 0, TK, K, E, ebits, cursor, row_token, pair_row);
+}
+
+// Multi-block path, step 1: per-chunk histograms bh[b][e].
+__global__ __launch_bounds__(kPermThreads) void beam_permute_hist(
+    const int32_t* __restrict__ ids, int TK, int E, int32_t* __restrict__ bh) {
+    __shared__ int hist[kMaxE];
+    const int tid = threadIdx.x;
+    if (tid < E) hist[tid] = 0;
+    __syncthreads();
+    const int begin = blockIdx.x * kPermChunk;
+    const int end = min(begin + kPermChunk, TK);
+    for (int p = begin + tid; p < end; p += kPermThreads) {
+        const int e = ids[p];
+        if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);
+    }
+    __syncthreads();
+    if (tid < E) bh[(size_t)blockIdx.x * E + tid] = hist[tid];
+}
+
+// Step 2 (one workgroup): expert offsets and each chunk's first row per expert.
+__global__ __launch_bounds__(kPermThreads) void beam_permute_scan(
+    const int32_t* __restrict__ bh, int nb, int TK, int E, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ bbase) {
+    __shared__ int tmp[4];
+    const int e = threadIdx.x;
+    int tot = 0;
+    if (e < E)
+        for (int b = 0; b < nb; ++b) tot += bh[(size_t)b * E + e];
+    int total;
+    const int excl = block_exclusive_scan(e < E ? tot : 0, tmp, &total);
+    if (e < E) {
+        offsets[e] = excl;
+        int run = excl;
+        for (int b = 0; b < nb; ++b) {
+            bbase[(size_t)b * E + e] = run;
+            run += bh[(size_t)b * E + e];
+        }
+    }
+    if (e == 0) offsets[E] = total;
+}
+
+// Step 3: stable scatter of each chunk from its per-expert base rows.
+__global__ __launch_bounds__(kPermThreads) void beam_permute_scatter(
+    const int32_t* __restrict__ ids, int TK, int K, int E, int ebits,
+    const int32_t* __restrict__ bbase, int32_t* __restrict__ row_token,
+    int32_t* __restrict__ pair_row) {
+    __shared__ int cursor[kMaxE];
+    const int tid = threadIdx.x;
+    if (tid < E) cursor[tid] = bbase[(size_t)blockIdx.x * E + tid];
+    __syncthreads();
+    const int begin = blockIdx.x * kPermChunk;
+    const int end = min(begin + kPermChunk, TK);
+    stable_scatter(ids, begin, end, K, E, ebits, cursor, row_token, pair_row);
+}
+
+// Dynamic per-token e4m3 quantisation of x: one workgroup per token row.
+__global__ __launch_bounds__(256) void beam_quantize_x_e4m3(
+    const uint16_t* __restrict__ x, int H, uint8_t* __restrict__ xq, float* __restrict__ xscale) {
+    __shared__ float red[4];
+    const size_t row = blockIdx.x;
+    const uint16_t* xr = x + row * H;
+    auto load4 = [&](int i) {
+        const uint2 u = *reinterpret_cast<const uint2*>(xr + i);
+        return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                           __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+    };
+    quantize_row_e4m3(load4, H, xq + row * H, xscale + row, red);
+}
+
+static int n_chunks(int TK) { return (TK + kPermChunk - 1) / kPermChunk; }
+
+size_t permute_ws_bytes(int T, int K, int E) {
+    const int nb = n_chunks(T * K);
+    return nb <= 1 ? 0 : 2 * (size_t)nb * E * sizeof(int32_t);
+}
+
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t st) {
+    const int TK = a.T * a.K;
+    int ebits = 0;
+    while ((1 << ebits) < a.E) ++ebits;
+    const int nb = n_chunks(TK);
+    if (nb <= 1) {
+        hipLaunchKernelGGL(beam_permute_fused, dim3(1), dim3(kPermThreads), 0, st, a.ids, TK, a.K,
+                           a.E, ebits, a.offsets, a.row_token, a.pair_row);
+    } else {
+        int32_t* bh = static_cast<int32_t*>(a.ws);
+        int32_t* bb = bh + (size_t)nb * a.E;
+        hipLaunchKernelGGL(beam_permute_hist, dim3(nb), dim3(kPermThreads), 0, st, a.ids, TK, a.E, bh);
+        hipLaunchKernelGGL(beam_permute_scan, dim3(1), dim3(kPermThreads), 0, st, bh, nb, TK, a.E,
+                           a.offsets, bb);
+        hipLaunchKernelGGL(beam_permute_scatter, dim3(nb), dim3(kPermThreads), 0, st, a.ids, TK, a.K,
+                           a.E, ebits, bb, a.row_token, a.pair_row);
+    }
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || a.xq == nullptr) return err;
+    hipLaunchKernelGGL(beam_quantize_x_e4m3, dim3(a.T), dim3(256), 0, st, a.x, a.H, a.xq, a.xscale);
+    return hipGetLastError();
+}
+
+}  // namespace beam

@@ -1,0 +1,314 @@
+// Router: FP32 logits (bf16 or fp32 activations x fp32 weights, fp32
+// accumulation), then sigmoid + correction bias + group-limited top-k +
+// renormalised weights in one wave per token.
+// (TokenSpeed x Reflection Beam blog, "Fused FP32 routing" and
+//  "Architecture"; vLLM Beam summary, MoE section.)
+#include "common.h"
+#include "kernels.h"
+
+namespace beam {
+
+template <typename XT> BEAM_DEV float ld_x(const XT* p);
+template <> BEAM_DEV float ld_x<float>(const float* p) { return *p; }
+template <> BEAM_DEV float ld_x<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+
+// 4 consecutive activations as fp32 (bf16 widened exactly)
+template <typename XT> BEAM_DEV float4 ld_x4(const XT* p);
+template <> BEAM_DEV float4 ld_x4<float>(const float* p) { return *reinterpret_cast<const float4*>(p); }
+template <> BEAM_DEV float4 ld_x4<uint16_t>(const uint16_t* p) {
+    uint2 v = *reinterpret_cast<const uint2*>(p);
+    return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+                       __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u));
+}
+
+// ---------------------------------------------------------------------------
+// Small-batch logits (T <= kSmallT): one workgroup per expert streams that
+// expert's router row once and forms the dot products of all tokens with it
+// (the pages' <=16-token GEMV design, re-tiled for 256-thread workgroups).
+// ---------------------------------------------------------------------------
+constexpr int kSmallT = 16;
+
+template <typename XT>
+__global__ __launch_bounds__(256) void beam_router_logits_small(
+    const XT* __restrict__ x, const float* __restrict__ w, float* __restrict__ logits,
+    int T, int H, int E) {
+    __shared__ float red[4][kSmallT];
+    const int e = blockIdx.x;
+    const float* wr = w + (size_t)e * H;
+    float acc[kSmallT];
+#pragma unroll
+    for (int t = 0; t < kSmallT; ++t) acc[t] = 0.f;
+    for (int k = threadIdx.x * 4; k < H; k += 1024) {
+        const float4 wv = *reinterpret_cast<const float4*>(wr + k);
+#pragma unroll
+        for (int t = 0; t < kSmallT; ++t) {
+            if (t < T) {
+                const float4 xv = ld_x4<XT>(x + (size_t)t * H + k);
+                acc[t] = fmaf(xv.x, wv.x, acc[t]);
+                acc[t] = fmaf(xv.y, wv.y, acc[t]);
+                acc[t] = fmaf(xv.z, wv.z, acc[t]);
+                acc[t] = fmaf(xv.w, wv.w, acc[t]);
+            }
+        }
+    }
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+    for (int t = 0; t < kSmallT; ++t) {
+        float s = wave_sum(acc[t]);
+        if (lane == 0) red[wv][t] = s;
+    }
+    __syncthreads();
+    if (threadIdx.x < T) {
+        const int t = threadIdx.x;
+        logits[(size_t)t * E + e] = (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Batched logits: C[T,E] = X[T,H] W[E,H]^T as an fp32 VALU GEMM.  Tile
+// 64 tokens x 64 experts per 256-thread workgroup, 4x4 outputs per thread,
+// K staged through LDS in chunks of 32 (k-major so each thread reads its
+// four tokens / four experts with one 16-byte LDS read).
+// ---------------------------------------------------------------------------
+constexpr int kLT = 64, kLE = 64, kLK = 32;
+
+template <typename XT>
+__global__ __launch_bounds__(256) void beam_router_logits_tiled(
+    const XT* __restrict__ x, const float* __restrict__ w, float* __restrict__ logits,
+    int T, int H, int E) {
+    __shared__ float xs[kLK][kLT + 4];
+    __shared__ float ws[kLK][kLE + 4];
+    const int t0 = blockIdx.x * kLT, e0 = blockIdx.y * kLE;
+    const int tid = threadIdx.x;
+    const int ty = tid >> 4, tx = tid & 15;
+    // loader mapping: each thread loads 8 consecutive k of one row
+    const int lr = tid >> 2, lk = (tid & 3) * 8;
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+
+    for (int k0 = 0; k0 < H; k0 += kLK) {
+        {
+            const int t = t0 + lr;
+            float v[8];
+            if (t < T) {
+                const float4 a = ld_x4<XT>(x + (size_t)t * H + k0 + lk);
+                const float4 b = ld_x4<XT>(x + (size_t)t * H + k0 + lk + 4);
+                v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+                v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[i] = 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) xs[lk + i][lr] = v[i];
+            const int e = e0 + lr;
+            if (e < E) {
+                const float4 a = *reinterpret_cast<const float4*>(w + (size_t)e * H + k0 + lk);
+                const float4 b = *reinterpret_cast<const float4*>(w + (size_t)e * H + k0 + lk + 4);
+                v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+                v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[i] = 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ws[lk + i][lr] = v[i];
+        }
+        __syncthreads();
+#pragma unroll 8
+        for (int k = 0; k < kLK; ++k) {
+            const float4 a = *reinterpret_cast<const float4*>(&xs[k][ty * 4]);
+            const float4 b = *reinterpret_cast<const float4*>(&ws[k][tx * 4]);
+            const float av[4] = {a.x, a.y, a.z, a.w};
+            const float bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int t = t0 + ty * 4 + i;
+        if (t >= T) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = e0 + tx * 4 + j;
+            if (e < E) logits[(size_t)t * E + e] = acc[i][j];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Selection: one wave per token.  Lane l holds experts [l*EPL, l*EPL+EPL);
+// a group of E/G experts spans LPG = E/G/EPL consecutive lanes.
+//   s = sigmoid(logit), b = s + bias (fp32)
+//   group score = sum of the `topn` largest b of the group (butterfly merge
+//   of sorted top-n lists inside the group's lanes)
+//   keep the `kg` best groups (ties: lower group)
+//   K rounds of a wave-wide arg-max over 64-bit keys (ordered(b) << 32 |
+//   ~expert) pick the experts in descending b, ties to the lower expert
+//   w_k = scale * s_k / sum_j s_j
+// ---------------------------------------------------------------------------
+constexpr int kMaxTopn = 4;
+
+template <int EPL>
+__global__ __launch_bounds__(256) void beam_route_select(
+    const float* __restrict__ logits, const float* __restrict__ bias,
+    int32_t* __restrict__ ids_out, float* __restrict__ w_out,
+    int T, int E, int G, int kg, int K, int topn, int lpg, float scale) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;   // whole wave exits together
+    const float* lg = logits + (size_t)t * E;
+
+    float s[EPL], b[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = lane * EPL + i;
+        if (e < E) {
+            const float z = lg[e];
+            s[i] = 1.0f / (1.0f + expf(-z));
+            b[i] = s[i] + bias[e];
+        } else {
+            s[i] = 0.f;
+            b[i] = -INFINITY;
+        }
+    }
+
+    // --- group score: top-n of the group's biased scores
+    float top[kMaxTopn];
+#pragma unroll
+    for (int j = 0; j < kMaxTopn; ++j) top[j] = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {          // insertion into a descending list
+        float v = b[i];
+#pragma unroll
+        for (int j = 0; j < kMaxTopn; ++j) {
+            const float hi = fmaxf(top[j], v), lo = fminf(top[j], v);
+            top[j] = hi;
+            v = lo;
+        }
+    }
+    for (int o = 1; o < lpg; o <<= 1) {      // merge with the partner lane's list
+        // both lists descend: max(a_j, b_{n-1-j}) is the top-n multiset
+        // (bitonic), then a half-cleaner network sorts it again
+        float c[kMaxTopn];
+#pragma unroll
+        for (int j = 0; j < kMaxTopn; ++j)
+            c[j] = fmaxf(top[j], __shfl_xor(top[kMaxTopn - 1 - j], o, kWave));
+#pragma unroll
+        for (int d = kMaxTopn / 2; d > 0; d >>= 1)
+#pragma unroll
+            for (int j = 0; j < kMaxTopn; ++j)
+                if ((j & d) == 0) {
+                    const float hi = fmaxf(c[j], c[j + d]), lo = fminf(c[j], c[j + d]);
+                    c[j] = hi;
+                    c[j + d] = lo;
+                }
+#pragma unroll
+        for (int j = 0; j < kMaxTopn; ++j) top[j] = c[j];
+    }
+    float gs = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxTopn; ++j)
+        if (j < topn) gs += top[j];
+
+    // --- keep the kg best groups
+    const int my_group = lane / lpg;
+    int rank = 0;
+    for (int g = 0; g < G; ++g) {
+        const float o = __shfl(gs, g * lpg, kWave);
+        rank += (o > gs) || (o == gs && g < my_group);
+    }
+    const bool group_kept = (my_group < G) && (rank < kg);
+
+    uint64_t key[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = lane * EPL + i;
+        key[i] = (group_kept && e < E)
+                     ? ((uint64_t)ordered_bits(b[i]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e)
+                     : 0ull;
+    }
+
+    // --- K rounds of wave arg-max
+    float my_s = 0.f, ssum = 0.f;
+    int my_id = 0;
+    for (int k = 0; k < K; ++k) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) best = key[i] > best ? key[i] : best;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const uint64_t other = __shfl_xor(best, o, kWave);
+            best = other > best ? other : best;
+        }
+        const int e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
+        const int owner = e / EPL, slot = e - owner * EPL;
+        float se = 0.f;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            if (i == slot) se = s[i];
+        se = __shfl(se, owner, kWave);
+        if (lane == owner) {
+#pragma unroll
+            for (int i = 0; i < EPL; ++i)
+                if (i == slot) key[i] = 0ull;
+        }
+        ssum += se;
+        if (lane == k) { my_s = se; my_id = e; }
+    }
+    if (lane < K) {
+        ids_out[(size_t)t * K + lane] = my_id;
+        w_out[(size_t)t * K + lane] = scale * my_s / ssum;
+    }
+}
+
+int route_epl(int E) { return E <= 64 ? 1 : (E <= 128 ? 2 : 4); }
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
+    const int T = a.T, H = a.H, E = a.E;
+    if (T <= kSmallT) {
+        if (a.x_bf16)
+            hipLaunchKernelGGL(beam_router_logits_small<uint16_t>, dim3(E), dim3(256), 0, st,
+                               (const uint16_t*)a.x, a.w, a.logits, T, H, E);
+        else
+            hipLaunchKernelGGL(beam_router_logits_small<float>, dim3(E), dim3(256), 0, st,
+                               (const float*)a.x, a.w, a.logits, T, H, E);
+    } else {
+        dim3 grid((T + kLT - 1) / kLT, (E + kLE - 1) / kLE);
+        if (a.x_bf16)
+            hipLaunchKernelGGL(beam_router_logits_tiled<uint16_t>, grid, dim3(256), 0, st,
+                               (const uint16_t*)a.x, a.w, a.logits, T, H, E);
+        else
+            hipLaunchKernelGGL(beam_router_logits_tiled<float>, grid, dim3(256), 0, st,
+                               (const float*)a.x, a.w, a.logits, T, H, E);
+    }
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int epl = route_epl(E);
+    const int lpg = (E / a.G) / epl;
+    dim3 grid((T + 3) / 4);
+    switch (epl) {
+        case 1:
+            hipLaunchKernelGGL(beam_route_select<1>, grid, dim3(256), 0, st, a.logits, a.bias, a.ids,
+                               a.wts, T, E, a.G, a.kg, a.K, a.topn, lpg, a.scale);
+            break;
+        case 2:
+            hipLaunchKernelGGL(beam_route_select<2>, grid, dim3(256), 0, st, a.logits, a.bias, a.ids,
+                               a.wts, T, E, a.G, a.kg, a.K, a.topn, lpg, a.scale);
+            break;
+        default:
+            hipLaunchKernelGGL(beam_route_select<4>, grid, dim3(256), 0, st, a.logits, a.bias, a.ids,
+                               a.wts, T, E, a.G, a.kg, a.K, a.topn, lpg, a.scale);
+            break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace beam

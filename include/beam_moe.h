@@ -1,0 +1,192 @@
+/*
+ * beam_moe.h -- C ABI of one Beam-style mixture-of-experts layer forward on
+ * an AMD Instinct MI355X (gfx950).
+ *
+ * The layer (TokenSpeed x Reflection Beam blog, section "Architecture";
+ * vLLM Beam summary, MoE and residual section):
+ *   route        FP32 router projection, sigmoid scores + per-expert
+ *                correction bias, group-limited top-k (4 of 8 groups, then
+ *                8 experts), renormalised weights times the routed scale 2.5
+ *   permute      stable expert-major grouping of the (token, slot) pairs,
+ *                plus optional dynamic per-token e4m3 quantisation of x
+ *   experts      grouped SwiGLU MLP per expert (GEMM1 + SwiGLU, GEMM2) in
+ *                bf16, fp8-e4m3 (per-channel weight scales, per-token
+ *                activation scales) or fp32
+ *   combine_norm weighted combine of the K expert outputs, post-RMSNorm,
+ *                depth-scaled residual h <- sqrt((n-1)/n) h + p / sqrt(n),
+ *                next pre-RMSNorm
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers, row-major, densely packed,
+ *     owned by the caller.  The library never allocates, frees, copies to
+ *     the host or synchronises; every call only enqueues kernels on
+ *     `stream` (a hipStream_t; NULL = the default stream) and returns.
+ *   - `cfg` is a host pointer, read during the call only.
+ *   - Arguments are validated before anything is enqueued: an invalid call
+ *     returns a non-zero status and enqueues nothing.  T == 0 returns
+ *     BEAM_OK and enqueues nothing.  A failed launch returns BEAM_ERR_HIP.
+ *   - `ws` is a caller-owned device workspace of at least
+ *     beam_moe_workspace_bytes(cfg, T, w_dtype) bytes.  One workspace may be
+ *     shared by the calls of one layer on one stream; calls that overlap in
+ *     time must not share one.
+ *   - Calls on one stream are ordered; the library keeps no state between
+ *     calls, so calls on different streams or threads are independent.
+ */
+#ifndef BEAM_MOE_H
+#define BEAM_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum beam_status {
+    BEAM_OK = 0,
+    BEAM_ERR_INVALID_ARG = 1,   /* null pointer, negative size, bad dtype     */
+    BEAM_ERR_UNSUPPORTED = 2,   /* shape the kernels are not built for        */
+    BEAM_ERR_WORKSPACE = 3,     /* ws missing or smaller than required         */
+    BEAM_ERR_HIP = 4            /* a kernel launch failed                      */
+} beam_status;
+
+typedef enum beam_dtype {
+    BEAM_F32 = 0,
+    BEAM_BF16 = 1,
+    BEAM_FP8_E4M3 = 2           /* OCP E4M3FN codes (uint8), max 448, no inf  */
+} beam_dtype;
+
+/* Layer shape.  Beam: {5120, 256, 8, 4, 8, 2, 2560, 2.5f, 1e-6f}. */
+typedef struct beam_moe_cfg {
+    int32_t hidden;        /* H: multiple of 256, at most 8192                 */
+    int32_t n_experts;     /* E: at most 256                                  */
+    int32_t n_groups;      /* G: E % G == 0; experts [g*E/G, (g+1)*E/G) form group g */
+    int32_t topk_groups;   /* groups kept per token, 1..G                     */
+    int32_t topk;          /* K experts per token, 1..min(32, topk_groups*E/G)*/
+    int32_t group_topn;    /* biased scores summed per group score, 1..min(4, E/G) */
+    int32_t d_ff;          /* F: multiple of 128 (256 for fp8 experts)         */
+    float routed_scale;    /* routing weights sum to this (2.5)               */
+    float rms_eps;         /* RMSNorm epsilon (1e-6)                           */
+} beam_moe_cfg;
+
+/*
+ * beam_moe_route -- router projection, scores, group-limited top-k, weights.
+ * (TokenSpeed blog, "Fused FP32 routing": bf16 activations times fp32 router
+ *  weights with fp32 accumulation and logits, then sigmoid, bias,
+ *  group top-k and the 2.5 scale folded into the weights.)
+ *
+ *   x          [T,H] activations, dtype x_dtype (BF16 or F32)
+ *   w_router   [E,H] fp32; row e produces expert e's logit
+ *   bias       [E]   fp32 correction bias (used for selection only)
+ *   topk_ids   [T,K] int32 out: chosen experts, descending biased score
+ *                    s+bias, ties to the lower expert index
+ *   topk_w     [T,K] fp32 out: routed_scale * s_k / sum_j s_j over the K
+ *                    chosen experts (s = sigmoid(logit), unbiased)
+ *   logits_out [T,E] fp32 out, nullable: the router logits
+ * Group score = sum of the group_topn largest biased scores of the group;
+ * the topk_groups best groups are kept (ties: lower group index).
+ */
+beam_status beam_moe_route(const beam_moe_cfg* cfg, int32_t T,
+                           const void* x, beam_dtype x_dtype,
+                           const float* w_router, const float* bias,
+                           int32_t* topk_ids, float* topk_w, float* logits_out,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * beam_moe_permute -- group the T*K (token, slot) pairs by expert.
+ * (vLLM Beam summary, kernel list: the MoE path's routing kernels that
+ *  group tokens by expert; TokenSpeed blog, "TensorRT-LLM NVFP4 MoE": input
+ *  quantisation does not depend on the routes.)
+ *
+ *   topk_ids        [T,K] int32 in (values in [0,E); pair p = t*K + k)
+ *   expert_offsets  [E+1] int32 out: exclusive prefix sum of per-expert
+ *                   pair counts (expert_offsets[E] = T*K)
+ *   row_token       [T*K] int32 out: permuted row r -> token t
+ *   pair_row        [T*K] int32 out: pair p -> permuted row r
+ *   Within one expert, rows follow ascending p (stable, unique).
+ *   x, x_dtype      [T,H] BF16 activations, read only when x_q != NULL
+ *   x_q             [T,H] uint8 out, nullable: e4m3 codes of x / x_scale[t]
+ *                   (round to nearest even, saturating at 448)
+ *   x_scale         [T] fp32 out (required with x_q): amax(|x[t]|) / 448,
+ *                   1 for an all-zero row
+ * Ids outside [0,E) are a caller error: they are not checked on the device.
+ */
+beam_status beam_moe_permute(const beam_moe_cfg* cfg, int32_t T,
+                             const int32_t* topk_ids,
+                             int32_t* expert_offsets, int32_t* row_token, int32_t* pair_row,
+                             const void* x, beam_dtype x_dtype,
+                             uint8_t* x_q, float* x_scale,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * beam_moe_experts -- grouped SwiGLU expert MLP over the permuted rows.
+ * (TokenSpeed blog, "TensorRT-LLM NVFP4 MoE": GEMM1 with SwiGLU fused,
+ *  then GEMM2; Gaudi cookbook, "What was built" and "EP vs TP quality":
+ *  per-channel FP8 weights, dynamic per-token activations, the
+ *  down-projection input quantised per token over the whole d_ff.)
+ *
+ * For permuted row r (expert e, token t = row_token[r]):
+ *   g = x[t] W_gu[e][0:F]^T,  v = x[t] W_gu[e][F:2F]^T,  a = silu(g) * v,
+ *   y[r] = a W_down[e]^T
+ *   w_dtype   F32: x F32, a kept fp32.   BF16: x BF16, a rounded to bf16.
+ *             FP8_E4M3: x is the e4m3 codes x_q with per-token x_scale from
+ *             beam_moe_permute; weights are e4m3 codes with per-output-row
+ *             fp32 scales; a is re-quantised per row over all F columns
+ *             (scale amax/448) before GEMM2.
+ *   x         [T,H] dtype per w_dtype (x_dtype must be F32, BF16 or FP8_E4M3
+ *             to match); x_scale [T] fp32 iff FP8
+ *   expert_offsets [E+1], row_token [T*K] from beam_moe_permute
+ *   w_gate_up [E,2F,H]: rows [0,F) gate, [F,2F) up; s_gate_up [E,2F] iff FP8
+ *   w_down    [E,H,F];                               s_down [E,H] iff FP8
+ *   y         [T*K,H] out, dtype y_dtype (F32 or BF16): unweighted expert
+ *             outputs in permuted row order
+ *   events    nullable array of 4 hipEvent_t recorded on `stream` before
+ *             GEMM1, after GEMM1, before GEMM2 and after GEMM2 (timing hook)
+ */
+beam_status beam_moe_experts(const beam_moe_cfg* cfg, int32_t T, beam_dtype w_dtype,
+                             const void* x, beam_dtype x_dtype, const float* x_scale,
+                             const int32_t* expert_offsets, const int32_t* row_token,
+                             const void* w_gate_up, const float* s_gate_up,
+                             const void* w_down, const float* s_down,
+                             void* y, beam_dtype y_dtype,
+                             void* ws, size_t ws_bytes, void* stream,
+                             void* const* events);
+
+/*
+ * beam_moe_combine_norm -- weighted combine + sandwich-norm boundary.
+ * (TokenSpeed blog, "MNNVL all-reduce and SandwichNorm fusion": post-norm,
+ *  depth-scaled residual and next pre-norm in one kernel; vLLM Beam
+ *  summary, kernel change 3: the same kernel combines the top-8 expert
+ *  outputs; MoE and residual section: h <- sqrt((n-1)/n) h + x / sqrt(n).)
+ *
+ * Per token t:
+ *   m      = sum_k topk_w[t,k] * y[pair_row[t*K+k]]            (fp32)
+ *   p      = round(m / sqrt(mean(m^2) + eps) * gamma_post)
+ *   h'     = round(sqrt((n-1)/n) * h[t] + p / sqrt(n))          -> h[t] (in place)
+ *   x_next = round(h' / sqrt(mean(h'^2) + eps) * gamma_pre)
+ * where round() is to act_dtype (BF16, or F32 = no rounding beyond fp32).
+ *   y [T*K,H] dtype y_dtype (F32|BF16); pair_row [T*K]; topk_w [T,K] fp32
+ *   h, x_next [T,H] act_dtype; gamma_post, gamma_pre [H] act_dtype
+ *   n        residual index >= 1 (n = 1 gives h' = p)
+ *   moe_out  [T,H] fp32 out, nullable: m
+ * h and x_next must not overlap.
+ */
+beam_status beam_moe_combine_norm(const beam_moe_cfg* cfg, int32_t T,
+                                  const void* y, beam_dtype y_dtype,
+                                  const int32_t* pair_row, const float* topk_w,
+                                  void* h, void* x_next, beam_dtype act_dtype,
+                                  const void* gamma_post, const void* gamma_pre,
+                                  int32_t n, float* moe_out, void* stream);
+
+/* Workspace bytes that route, permute and experts need for T tokens with
+ * experts of w_dtype (the maximum over the three).  0 for invalid input. */
+size_t beam_moe_workspace_bytes(const beam_moe_cfg* cfg, int32_t T, beam_dtype w_dtype);
+
+/* Static, human-readable name of a status code. */
+const char* beam_moe_status_string(beam_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BEAM_MOE_H */

@@ -1,0 +1,145 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched):
+the library loads and exports every function the header declares, and
+invalid calls are rejected with the documented status before anything is
+enqueued."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "beam_moe.h")
+
+beam = pytest.importorskip("expert_routed_ffn_amd")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(beam.LIB_PATH):
+        pytest.skip("library not built")
+    return beam.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(beam_moe_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_layer_calls():
+    d = _declared()
+    for name in ("beam_moe_route", "beam_moe_permute", "beam_moe_experts", "beam_moe_combine_norm",
+                 "beam_moe_workspace_bytes", "beam_moe_status_string"):
+        assert name in d
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in _declared():
+        assert hasattr(L, name), name
+    assert sorted(beam.SYMBOLS) == _declared()
+
+
+def test_status_strings(L):
+    for code, text in beam.STATUS.items():
+        assert L.beam_moe_status_string(code).decode() == text
+    assert L.beam_moe_status_string(99).decode() == "unknown status"
+
+
+def _cfg(**kw):
+    return beam.LayerCfg(**kw).c()
+
+
+FAKE = 0x10000   # never dereferenced: every call below fails validation first
+
+
+def _route(L, cfg, T=8, x=FAKE, x_dt=beam.BEAM_BF16, w=FAKE, b=FAKE, ids=FAKE, wt=FAKE, lg=None,
+           ws=FAKE, wsb=1 << 30):
+    return L.beam_moe_route(ctypes.byref(cfg), T, x, x_dt, w, b, ids, wt, lg, ws, wsb, None)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(hidden=100), dict(hidden=8448), dict(n_experts=512), dict(n_groups=3),
+    dict(topk_groups=9), dict(topk=33), dict(group_topn=5), dict(d_ff=100),
+    dict(routed_scale=0.0), dict(rms_eps=-1.0), dict(topk=0), dict(n_experts=256, n_groups=256, topk_groups=4),
+])
+def test_invalid_cfg_rejected(L, bad):
+    st = _route(L, _cfg(**bad))
+    assert st in (1, 2), (bad, st)
+
+
+def test_route_argument_checks(L):
+    c = _cfg()
+    assert _route(L, c, T=-1) == 1
+    assert _route(L, c, x=None) == 1
+    assert _route(L, c, ids=None) == 1
+    assert _route(L, c, x_dt=beam.BEAM_FP8_E4M3) == 1
+    assert _route(L, c, x=FAKE + 2) == 1                    # misaligned
+    assert _route(L, c, ws=None) == 3                       # logits need workspace
+    assert _route(L, c, wsb=16) == 3
+    assert L.beam_moe_route(None, 8, FAKE, 1, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == 1
+
+
+def test_zero_tokens_is_a_no_op(L):
+    c = _cfg()
+    # T == 0 returns before touching any pointer (all null here)
+    assert L.beam_moe_route(ctypes.byref(c), 0, None, 1, None, None, None, None, None, None, 0, None) == 0
+    assert L.beam_moe_permute(ctypes.byref(c), 0, None, None, None, None, None, 1, None, None, None, 0, None) == 0
+    assert L.beam_moe_experts(ctypes.byref(c), 0, 1, None, 1, None, None, None, None, None, None, None,
+                              None, 0, None, 0, None, None) == 0
+    assert L.beam_moe_combine_norm(ctypes.byref(c), 0, None, 0, None, None, None, None, 1, None, None,
+                                   1, None, None) == 0
+
+
+def test_permute_argument_checks(L):
+    c = _cfg()
+    f = lambda **kw: L.beam_moe_permute(
+        ctypes.byref(c), kw.get("T", 8), kw.get("ids", FAKE), FAKE, FAKE, FAKE, kw.get("x", None),
+        kw.get("xdt", 1), kw.get("xq", None), kw.get("xs", None), kw.get("ws", None), kw.get("wsb", 0), None)
+    assert f(ids=None) == 1
+    assert f(xq=FAKE) == 1                 # x_q needs x and x_scale
+    assert f(xq=FAKE, x=FAKE, xs=FAKE, xdt=0) == 1
+    assert f(T=4096) == 3                  # multi-block permutation needs workspace
+
+
+def test_experts_argument_checks(L):
+    c = _cfg()
+
+    def f(T=8, w_dt=1, x_dt=1, xs=None, sgu=None, sd=None, y_dt=0, ws=FAKE, wsb=1 << 40, x=FAKE, y=FAKE):
+        return L.beam_moe_experts(ctypes.byref(c), T, w_dt, x, x_dt, xs, FAKE, FAKE, FAKE, sgu, FAKE,
+                                  sd, y, y_dt, ws, wsb, None, None)
+
+    assert f(x_dt=0) == 1                      # activation dtype must match the weights
+    assert f(y_dt=2) == 1                      # y cannot be fp8
+    assert f(w_dt=2, x_dt=2) == 1              # fp8 needs scales
+    assert f(ws=None) == 3
+    assert f(wsb=1024) == 3
+    assert f(x=None) == 1
+    assert f(y=FAKE + 4) == 1
+    assert f(w_dt=7, x_dt=7) == 1
+
+
+def test_combine_argument_checks(L):
+    c = _cfg()
+
+    def f(n=20, y_dt=0, a_dt=1, h=FAKE, xn=FAKE + 4096):
+        return L.beam_moe_combine_norm(ctypes.byref(c), 8, FAKE, y_dt, FAKE, FAKE, h, xn, a_dt, FAKE,
+                                       FAKE, n, None, None)
+
+    assert f(n=0) == 1
+    assert f(y_dt=2) == 1
+    assert f(a_dt=2) == 1
+    assert f(h=None) == 1
+    assert f(xn=FAKE) == 1                     # x_next must not alias h
+
+
+def test_workspace_bytes(L):
+    c = _cfg()
+    sizes = [L.beam_moe_workspace_bytes(ctypes.byref(c), T, 1) for T in (1, 8, 64, 2048, 16384)]
+    assert all(s > 0 for s in sizes)
+    assert sizes == sorted(sizes)
+    # fp8 keeps an fp32 intermediate plus codes
+    assert L.beam_moe_workspace_bytes(ctypes.byref(c), 16384, 2) > sizes[-1]
+    assert L.beam_moe_workspace_bytes(ctypes.byref(c), -1, 1) == 0
+    assert L.beam_moe_workspace_bytes(ctypes.byref(_cfg(hidden=100)), 8, 1) == 0
