@@ -203,6 +203,9 @@ beam_status beam_moe_combine_norm(const beam_moe_cfg* cfg, int32_t T, const void
     if (!y || !pair_row || !topk_w || !h || !x_next || !gamma_post || !gamma_pre)
         return BEAM_ERR_INVALID_ARG;
     if (h == x_next) return BEAM_ERR_INVALID_ARG;
+    if (!aligned16(y) || !aligned16(h) || !aligned16(x_next) || !aligned16(gamma_post) ||
+        !aligned16(gamma_pre) || (moe_out && !aligned16(moe_out)))
+        return BEAM_ERR_INVALID_ARG;
     beam::CombineArgs a{};
     a.T = T;
     a.K = cfg->topk;

@@ -5,55 +5,69 @@
 //  residual section: h <- sqrt((n-1)/n) h + x/sqrt(n), fp32 math with the
 //  bf16 rounding points of the reference.)
 //
-// One 256-thread workgroup per token; thread i owns elements i, i+256, ...
-// of the hidden row, so every global access is a coalesced row segment.
+// One 256-thread workgroup per token; thread i owns the 4-element chunks
+// i, i+256, ... of the hidden row, so every global access is a coalesced
+// row segment, and the K expert rows of a token are read with all their
+// loads in flight together.
 #include "common.h"
 #include "kernels.h"
 
 namespace beam {
 
-constexpr int kMaxIt = 32;   // H <= 32 * 256
+constexpr int kMaxIt = 8;    // chunks of 4 per thread: H <= 8 * 1024
 constexpr int kMaxK = 32;
 
-template <bool BF> BEAM_DEV float ld_act(const void* p, size_t i) {
-    if constexpr (BF) return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
-    else return static_cast<const float*>(p)[i];
+// 4 consecutive elements as fp32
+template <bool BF> BEAM_DEV float4 ld4(const void* p, size_t i) {
+    if constexpr (BF) {
+        const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+        return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                           __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+    } else {
+        return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+    }
 }
 template <bool BF> BEAM_DEV float rnd_act(float v) {
     if constexpr (BF) return bf16_to_f32(f32_to_bf16(v));
     else return v;
 }
-template <bool BF> BEAM_DEV void st_act(void* p, size_t i, float v) {
-    if constexpr (BF) static_cast<uint16_t*>(p)[i] = f32_to_bf16(v);
-    else static_cast<float*>(p)[i] = v;
+template <bool BF> BEAM_DEV void st4(void* p, size_t i, float4 v) {
+    if constexpr (BF) {
+        const uint32_t a = f32_to_bf16(v.x) | (uint32_t(f32_to_bf16(v.y)) << 16);
+        const uint32_t b = f32_to_bf16(v.z) | (uint32_t(f32_to_bf16(v.w)) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p) + i) = make_uint2(a, b);
+    } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(p) + i) = v;
+    }
 }
 
+BEAM_DEV float4 fma4(float w, float4 y, float4 m) {
+    return make_float4(fmaf(w, y.x, m.x), fmaf(w, y.y, m.y), fmaf(w, y.z, m.z), fmaf(w, y.w, m.w));
+}
+
+// One workgroup per token; thread i owns the 4-element chunks i, i+256, ...
 template <bool YBF, bool ABF>
 __global__ __launch_bounds__(256) void beam_combine_norm(CombineArgs a) {
-    __shared__ int rows_s[kMaxK];
-    __shared__ float w_s[kMaxK];
     __shared__ float red[4];
     const int t = blockIdx.x, tid = threadIdx.x;
     const int H = a.H, K = a.K;
     const int TK = a.T * K;
-    if (tid < K) {
-        rows_s[tid] = a.pair_row[(size_t)t * K + tid];
-        w_s[tid] = a.w[(size_t)t * K + tid];
-    }
-    __syncthreads();
+    const int32_t* prow = a.pair_row + (size_t)t * K;
+    const float* wrow = a.w + (size_t)t * K;
 
-    float m[kMaxIt];
+    float4 m[kMaxIt];
 #pragma unroll
-    for (int it = 0; it < kMaxIt; ++it) m[it] = 0.f;
+    for (int it = 0; it < kMaxIt; ++it) m[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
     for (int k = 0; k < K; ++k) {
-        const int r = rows_s[k];
+        const int r = prow[k];
         if ((unsigned)r >= (unsigned)TK) continue;   // never read outside y
-        const float wk = w_s[k];
+        const float wk = wrow[k];
         const size_t base = (size_t)r * H;
 #pragma unroll
         for (int it = 0; it < kMaxIt; ++it) {
-            const int i = it * 256 + tid;
-            if (i < H) m[it] = fmaf(wk, ld_act<YBF>(a.y, base + i), m[it]);
+            const int i = (it * 256 + tid) * 4;
+            if (i < H) m[it] = fma4(wk, ld4<YBF>(a.y, base + i), m[it]);
         }
     }
 
@@ -61,32 +75,41 @@ __global__ __launch_bounds__(256) void beam_combine_norm(CombineArgs a) {
     float ss = 0.f;
 #pragma unroll
     for (int it = 0; it < kMaxIt; ++it)
-        if (it * 256 + tid < H) ss = fmaf(m[it], m[it], ss);
+        if ((it * 256 + tid) * 4 < H)
+            ss += (m[it].x * m[it].x + m[it].y * m[it].y) + (m[it].z * m[it].z + m[it].w * m[it].w);
     ss = block_sum<4>(ss, red);
     const float rinv = 1.0f / sqrtf(ss / (float)H + a.eps);
 
-    // residual update (h' overwrites m)
+    // residual update; h' replaces m
     const size_t rowo = (size_t)t * H;
     float ss2 = 0.f;
 #pragma unroll
     for (int it = 0; it < kMaxIt; ++it) {
-        const int i = it * 256 + tid;
+        const int i = (it * 256 + tid) * 4;
         if (i < H) {
-            if (a.moe_out) a.moe_out[rowo + i] = m[it];
-            const float p = rnd_act<ABF>(m[it] * rinv * ld_act<ABF>(a.gpost, i));
-            const float hn = rnd_act<ABF>(a.c_res * ld_act<ABF>(a.h, rowo + i) + a.c_new * p);
+            if (a.moe_out) *reinterpret_cast<float4*>(a.moe_out + rowo + i) = m[it];
+            const float4 g = ld4<ABF>(a.gpost, i);
+            const float4 h = ld4<ABF>(a.h, rowo + i);
+            float4 hn;
+            hn.x = rnd_act<ABF>(a.c_res * h.x + a.c_new * rnd_act<ABF>(m[it].x * rinv * g.x));
+            hn.y = rnd_act<ABF>(a.c_res * h.y + a.c_new * rnd_act<ABF>(m[it].y * rinv * g.y));
+            hn.z = rnd_act<ABF>(a.c_res * h.z + a.c_new * rnd_act<ABF>(m[it].z * rinv * g.z));
+            hn.w = rnd_act<ABF>(a.c_res * h.w + a.c_new * rnd_act<ABF>(m[it].w * rinv * g.w));
             m[it] = hn;
-            ss2 = fmaf(hn, hn, ss2);
+            ss2 += (hn.x * hn.x + hn.y * hn.y) + (hn.z * hn.z + hn.w * hn.w);
         }
     }
     ss2 = block_sum<4>(ss2, red);
     const float rinv2 = 1.0f / sqrtf(ss2 / (float)H + a.eps);
 #pragma unroll
     for (int it = 0; it < kMaxIt; ++it) {
-        const int i = it * 256 + tid;
+        const int i = (it * 256 + tid) * 4;
         if (i < H) {
-            st_act<ABF>(a.h, rowo + i, m[it]);
-            st_act<ABF>(a.x_next, rowo + i, m[it] * rinv2 * ld_act<ABF>(a.gpre, i));
+            st4<ABF>(a.h, rowo + i, m[it]);
+            const float4 g = ld4<ABF>(a.gpre, i);
+            st4<ABF>(a.x_next, rowo + i,
+                     make_float4(m[it].x * rinv2 * g.x, m[it].y * rinv2 * g.y, m[it].z * rinv2 * g.z,
+                                 m[it].w * rinv2 * g.w));
         }
     }
 }

@@ -32,30 +32,42 @@ template <typename XT>
 __global__ __launch_bounds__(256) void beam_router_logits_small(
     const XT* __restrict__ x, const float* __restrict__ w, float* __restrict__ logits,
     int T, int H, int E) {
+    constexpr int kMaxIt = 8;   // H <= 8 * 1024
     __shared__ float red[4][kSmallT];
     const int e = blockIdx.x;
     const float* wr = w + (size_t)e * H;
+    // all of this thread's router weights first (one latency for the row)
+    float4 wv[kMaxIt];
+#pragma unroll
+    for (int it = 0; it < kMaxIt; ++it) {
+        const int k = (it * 256 + threadIdx.x) * 4;
+        wv[it] = k < H ? *reinterpret_cast<const float4*>(wr + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     float acc[kSmallT];
 #pragma unroll
-    for (int t = 0; t < kSmallT; ++t) acc[t] = 0.f;
-    for (int k = threadIdx.x * 4; k < H; k += 1024) {
-        const float4 wv = *reinterpret_cast<const float4*>(wr + k);
+    for (int t = 0; t < kSmallT; ++t) {
+        acc[t] = 0.f;
+        if (t < T) {
 #pragma unroll
-        for (int t = 0; t < kSmallT; ++t) {
-            if (t < T) {
-                const float4 xv = ld_x4<XT>(x + (size_t)t * H + k);
-                acc[t] = fmaf(xv.x, wv.x, acc[t]);
-                acc[t] = fmaf(xv.y, wv.y, acc[t]);
-                acc[t] = fmaf(xv.z, wv.z, acc[t]);
-                acc[t] = fmaf(xv.w, wv.w, acc[t]);
+            for (int it = 0; it < kMaxIt; ++it) {
+                const int k = (it * 256 + threadIdx.x) * 4;
+                if (k < H) {
+                    const float4 xv = ld_x4<XT>(x + (size_t)t * H + k);
+                    acc[t] = fmaf(xv.x, wv[it].x, acc[t]);
+                    acc[t] = fmaf(xv.y, wv[it].y, acc[t]);
+                    acc[t] = fmaf(xv.z, wv[it].z, acc[t]);
+                    acc[t] = fmaf(xv.w, wv[it].w, acc[t]);
+                }
             }
         }
     }
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wq = threadIdx.x >> 6;
 #pragma unroll
     for (int t = 0; t < kSmallT; ++t) {
-        float s = wave_sum(acc[t]);
-        if (lane == 0) red[wv][t] = s;
+        if (t < T) {
+            const float s = wave_sum(acc[t]);
+            if (lane == 0) red[wq][t] = s;
+        }
     }
     __syncthreads();
     if (threadIdx.x < T) {
