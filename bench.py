@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--workload", default="decode_t8")
     ap.add_argument("--all", action="store_true", help="also time the other Beam workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=4)
+    ap.add_argument("--cpu-tokens", type=int, default=8)
     return ap.parse_args()
 
 
@@ -79,6 +79,23 @@ class HipEvents:
 
 def kernel_hash():
     return hashlib.sha256(open(EXPERTS_SRC, "rb").read()).hexdigest()[:16]
+
+
+def lcfg(wl):
+    import expert_routed_ffn_amd as beam
+    return beam.LayerCfg(wl.hidden, wl.n_experts, wl.n_groups, wl.topk_groups, wl.topk,
+                         wl.group_topn, wl.d_ff, wl.routed_scale, wl.rms_eps)
+
+
+def packed_stacks(wl, dev):
+    """All experts' weights in the packed layout the expert GEMM reads
+    (built once, before any timing)."""
+    import torch
+    import expert_routed_ffn_amd as beam
+    import synth
+    st = beam.packed_expert_stacks(lcfg(wl), lambda e: synth.make_expert(wl, e, dev), wl.n_experts, dev)
+    torch.cuda.synchronize()
+    return st
 
 
 def layer_setup(wl, stacks, dev):
@@ -161,10 +178,12 @@ def traffic_for(workload, kernel):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, state, n_tokens):
-    """Times the CPU oracle on the first n_tokens tokens of the workload
-    (host-resident weights of the experts they use; the oracle widens them
-    to fp64 itself as part of its work)."""
+def cpu_baseline(wl, state, n_tokens, min_seconds=10.0, max_reps=8):
+    """Times the CPU oracle on the first n_tokens tokens of the workload (all
+    of them for the decode shape), repeating the pass until at least
+    min_seconds of CPU work have been timed.  The experts' plain bf16 weights
+    are staged on the host before the clock starts; the oracle widens them
+    to fp64 itself as part of its work."""
     import numpy as np
     import torch
     import oracle
@@ -179,24 +198,30 @@ def cpu_baseline(wl, state, n_tokens):
                 hidden=wl.hidden, d_ff=wl.d_ff, rms_eps=wl.rms_eps)
     routes = oracle.route(oracle.router_logits(xn, w_r), bias, ocfg)
     need = sorted({int(e) for r in routes for e in r.ids})
-    host = {e: (s["wgu"][e].cpu(), s["wd"][e].cpu()) for e in need}   # staged, not timed
+    # plain row-major weights of the needed experts, staged on the host before the clock
+    host = {}
+    for e in need:
+        a, b, c, d = synth.make_expert(wl, e, s["x"].device)
+        host[e] = (a.cpu(), b.cpu(), None if c is None else synth.to_f64(c), None if d is None else synth.to_f64(d))
     fp8 = wl.w_dtype == "fp8"
     if fp8:
-        sc = {e: (synth.to_f64(s["sgu"][e]), synth.to_f64(s["sd"][e])) for e in need}
-        ew = lambda e: {"q_gu": host[e][0].numpy(), "s_gu": sc[e][0], "q_d": host[e][1].numpy(), "s_d": sc[e][1]}
+        ew = lambda e: {"q_gu": host[e][0].numpy(), "s_gu": host[e][2], "q_d": host[e][1].numpy(), "s_d": host[e][3]}
     else:
         ew = lambda e: {"w_gu": host[e][0].to(torch.float64).numpy(), "w_d": host[e][1].to(torch.float64).numpy()}
     h = synth.to_f64(s["h0"])[tokens]
     gp, gq = synth.to_f64(s["gp"]), synth.to_f64(s["gq"])
-    t0 = time.perf_counter()
-    oracle.layer_tokens(ocfg, xn, w_r, bias, ew, h, gp, gq, wl.n, w_dtype=wl.w_dtype,
-                        rnd=oracle.round_bf16)
-    dt = time.perf_counter() - t0
+    reps, dt = 0, 0.0
+    while reps < max_reps and (reps == 0 or dt < min_seconds):
+        t0 = time.perf_counter()
+        oracle.layer_tokens(ocfg, xn, w_r, bias, ew, h, gp, gq, wl.n, w_dtype=wl.w_dtype,
+                            rnd=oracle.round_bf16)
+        dt += time.perf_counter() - t0
+        reps += 1
     cores = len(os.sched_getaffinity(0))
-    return {"value": len(tokens) / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{len(tokens)} of the {wl.T} tokens of {wl.name}: full layer (router, "
-                      f"selection, {len(need)} experts' SwiGLU MLPs in fp64, combine, norm boundary); "
-                      f"{dt:.1f} s on {cores} host threads"}
+    return {"value": len(tokens) * reps / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(tokens)} of the {wl.T} tokens of {wl.name} through the whole layer (router, "
+                      f"selection, the {len(need)} experts they use as fp64 SwiGLU MLPs, combine, norm "
+                      f"boundary), {reps} passes, {dt:.1f} s on {cores} host threads"}
 
 
 def main():
@@ -221,7 +246,7 @@ def main():
     hipev = HipEvents()
 
     wl = synth.WORKLOADS[args.workload]
-    stacks = synth.make_expert_stacks(wl, dev)
+    stacks = packed_stacks(wl, dev)
     torch.cuda.synchronize()
     r = time_workload(wl, stacks, args.steps, args.warmup, hipev, dev)
     D = r["touched"]
@@ -272,7 +297,7 @@ def main():
         for name in names:
             w2 = synth.WORKLOADS[name]
             if w2.w_dtype not in by_dtype:
-                by_dtype[w2.w_dtype] = synth.make_expert_stacks(w2, dev)
+                by_dtype[w2.w_dtype] = packed_stacks(w2, dev)
             r2 = time_workload(w2, by_dtype[w2.w_dtype], max(3, args.steps // 5), 2, hipev, dev)
             a2 = algorithmic(w2, r2["touched"])
             fl = a2["g1_flops"] + a2["g2_flops"]

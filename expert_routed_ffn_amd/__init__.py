@@ -29,7 +29,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape or dtype",
           3: "workspace missing or too small", 4: "HIP launch failed"}
 
 SYMBOLS = ("beam_moe_route", "beam_moe_permute", "beam_moe_experts", "beam_moe_combine_norm",
-           "beam_moe_workspace_bytes", "beam_moe_status_string")
+           "beam_moe_pack_weights", "beam_moe_workspace_bytes", "beam_moe_status_string")
 
 
 class BeamMoeCfg(ctypes.Structure):
@@ -83,11 +83,13 @@ def lib() -> ctypes.CDLL:
     L.beam_moe_experts.argtypes = [cfgp, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32,
                                    vp, sz, vp, vp]
     L.beam_moe_combine_norm.argtypes = [cfgp, i32, vp, i32, vp, vp, vp, vp, i32, vp, vp, i32, vp, vp]
+    L.beam_moe_pack_weights.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp]
     L.beam_moe_workspace_bytes.argtypes = [cfgp, i32, i32]
     L.beam_moe_workspace_bytes.restype = sz
     L.beam_moe_status_string.argtypes = [i32]
     L.beam_moe_status_string.restype = ctypes.c_char_p
-    for f in ("beam_moe_route", "beam_moe_permute", "beam_moe_experts", "beam_moe_combine_norm"):
+    for f in ("beam_moe_route", "beam_moe_permute", "beam_moe_experts", "beam_moe_combine_norm",
+              "beam_moe_pack_weights"):
         getattr(L, f).restype = i32
     _lib = L
     return L
@@ -227,6 +229,43 @@ def beam_moe_combine_norm(cfg: LayerCfg, y, pair_row, topk_w, h, x_next, gamma_p
     _ok("beam_moe_combine_norm", st)
 
 
+def beam_moe_pack_weights(cfg: LayerCfg, w_gate_up, w_down, packed_gate_up, packed_down, stream=None):
+    """Re-lays out [n,2F,H] / [n,H,F] expert stacks into the tiled layout that
+    beam_moe_experts reads (any n >= 1 experts)."""
+    n = w_gate_up.shape[0]
+    H, F = cfg.hidden, cfg.d_ff
+    dt = w_gate_up.dtype
+    _check(w_gate_up, (n, 2 * F, H), (dt,), "w_gate_up")
+    _check(w_down, (n, H, F), (dt,), "w_down")
+    _check(packed_gate_up, (n, 2 * F, H), (dt,), "packed_gate_up")
+    _check(packed_down, (n, H, F), (dt,), "packed_down")
+    st = lib().beam_moe_pack_weights(ctypes.byref(cfg.c()), n, _dt(w_gate_up), _p(w_gate_up), _p(w_down),
+                                     _p(packed_gate_up), _p(packed_down), _stream(stream))
+    _ok("beam_moe_pack_weights", st)
+
+
+def packed_expert_stacks(cfg: LayerCfg, make_expert, n_experts: int, device="cuda"):
+    """Builds packed [E,2F,H] / [E,H,F] stacks one expert at a time from
+    make_expert(e) -> (w_gate_up [2F,H], w_down [H,F], s_gate_up, s_down)
+    device tensors.  Returns (packed_gate_up, packed_down, s_gate_up, s_down)."""
+    H, F = cfg.hidden, cfg.d_ff
+    a, b, c, d = make_expert(0)
+    pgu = torch.empty((n_experts, 2 * F, H), dtype=a.dtype, device=device)
+    pd = torch.empty((n_experts, H, F), dtype=b.dtype, device=device)
+    sgu = sd = None
+    if c is not None:
+        sgu = torch.empty((n_experts, 2 * F), dtype=torch.float32, device=device)
+        sd = torch.empty((n_experts, H), dtype=torch.float32, device=device)
+    for e in range(n_experts):
+        if e:
+            a, b, c, d = make_expert(e)
+        beam_moe_pack_weights(cfg, a.unsqueeze(0), b.unsqueeze(0), pgu[e:e + 1], pd[e:e + 1])
+        if sgu is not None:
+            sgu[e].copy_(c)
+            sd[e].copy_(d)
+    return pgu, pd, sgu, sd
+
+
 # ------------------------------------------------------------------ whole layer
 
 @dataclasses.dataclass
@@ -269,8 +308,9 @@ def alloc_buffers(cfg: LayerCfg, T: int, act_dtype, w_dtype: int, y_dtype=torch.
 
 def moe_layer(cfg: LayerCfg, x, w_router, bias, w_gate_up, w_down, h, gamma_post, gamma_pre, n,
               bufs: LayerBuffers, s_gate_up=None, s_down=None, stream=None, events=None):
-    """Runs the four entry points in order on one stream.  h is updated in
-    place; the other results land in `bufs`."""
+    """Runs the four entry points in order on one stream.  w_gate_up/w_down
+    are packed stacks (beam_moe_pack_weights).  h is updated in place; the
+    other results land in `bufs`."""
     T = x.shape[0]
     fp8 = _dt(w_gate_up) == BEAM_FP8_E4M3
     beam_moe_route(cfg, x, w_router, bias, bufs.topk_ids, bufs.topk_w, bufs.logits, bufs.ws, stream)

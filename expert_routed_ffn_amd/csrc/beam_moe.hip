@@ -190,6 +190,43 @@ beam_status beam_moe_experts(const beam_moe_cfg* cfg, int32_t T, beam_dtype w_dt
                                                                                     : BEAM_ERR_HIP;
 }
 
+beam_status beam_moe_pack_weights(const beam_moe_cfg* cfg, int32_t n_experts, beam_dtype w_dtype,
+                                  const void* w_gate_up, const void* w_down, void* packed_gate_up,
+                                  void* packed_down, void* stream) {
+    // packing only depends on the matrix shapes (hidden, d_ff)
+    if (!cfg || cfg->hidden <= 0 || cfg->d_ff <= 0) return BEAM_ERR_INVALID_ARG;
+    if (cfg->hidden % 256 != 0 || cfg->hidden > 8192 || cfg->d_ff % 128 != 0 || cfg->d_ff > 8192)
+        return BEAM_ERR_UNSUPPORTED;
+    if (n_experts < 0 || !valid_dtype(w_dtype)) return BEAM_ERR_INVALID_ARG;
+    if (w_dtype == BEAM_FP8_E4M3 && (cfg->hidden % 256 != 0 || cfg->d_ff % 256 != 0))
+        return BEAM_ERR_UNSUPPORTED;
+    if (n_experts == 0) return BEAM_OK;
+    if (!w_gate_up || !w_down || !packed_gate_up || !packed_down) return BEAM_ERR_INVALID_ARG;
+    if (!aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(packed_gate_up) || !aligned16(packed_down))
+        return BEAM_ERR_INVALID_ARG;
+    const size_t es = w_dtype == BEAM_F32 ? 4 : (w_dtype == BEAM_BF16 ? 2 : 1);
+    const size_t H = cfg->hidden, F = cfg->d_ff, E = (size_t)n_experts;
+    const size_t gu_bytes = E * 2 * F * H * es, d_bytes = E * H * F * es;
+    auto overlap = [](const void* a, size_t na, const void* b, size_t nb) {
+        const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+        return x < y + nb && y < x + na;
+    };
+    if (overlap(w_gate_up, gu_bytes, packed_gate_up, gu_bytes) || overlap(w_down, d_bytes, packed_down, d_bytes) ||
+        overlap(packed_gate_up, gu_bytes, packed_down, d_bytes))
+        return BEAM_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err;
+    if (w_dtype == BEAM_F32) {   // the fp32 path reads plain row-major weights
+        err = hipMemcpyAsync(packed_gate_up, w_gate_up, gu_bytes, hipMemcpyDeviceToDevice, s);
+        if (err == hipSuccess)
+            err = hipMemcpyAsync(packed_down, w_down, d_bytes, hipMemcpyDeviceToDevice, s);
+    } else {
+        err = beam::launch_pack(w_gate_up, packed_gate_up, E * 2 * F, (int)(H * es), s);
+        if (err == hipSuccess) err = beam::launch_pack(w_down, packed_down, E * H, (int)(F * es), s);
+    }
+    return err == hipSuccess ? BEAM_OK : BEAM_ERR_HIP;
+}
+
 beam_status beam_moe_combine_norm(const beam_moe_cfg* cfg, int32_t T, const void* y,
                                   beam_dtype y_dtype, const int32_t* pair_row, const float* topk_w,
                                   void* h, void* x_next, beam_dtype act_dtype, const void* gamma_post,

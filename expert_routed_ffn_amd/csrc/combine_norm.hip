@@ -15,7 +15,6 @@
 namespace beam {
 
 constexpr int kMaxIt = 8;    // chunks of 4 per thread: H <= 8 * 1024
-constexpr int kMaxK = 32;
 
 // 4 consecutive elements as fp32
 template <bool BF> BEAM_DEV float4 ld4(const void* p, size_t i) {

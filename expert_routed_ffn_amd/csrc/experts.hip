@@ -14,10 +14,12 @@
 // 16 matching up rows, so SwiGLU happens in registers; GEMM2: 32 output
 // rows) and the item's rows in blocks of 16.  Weights stream from HBM
 // straight into MFMA A-operand registers, each weight byte read once per
-// item; activation rows (few, L2-resident) are the B operand.  Per K step a
-// lane loads 64 contiguous bytes of its weight row, so a wave reads 16 rows
-// x 256 contiguous bytes; the MFMA's k index is permuted consistently
-// between A and B to allow that.
+// item, from the packed layout (pack.hip): every weight load instruction of
+// a wave reads 1 KiB of contiguous whole cache lines, non-temporally.
+// Activation rows (few, L2-resident) are the B operand; lane (r, g) reads
+// bytes [64 s + 16 g, +16) of its row for piece s, the same k bytes the
+// packed A fragment holds.  bf16: MFMA step s uses piece s.  fp8: MFMA step
+// t uses pieces 2t and 2t+1 (32 bytes = the lane's 32 k values).
 #include "common.h"
 #include "kernels.h"
 
@@ -25,7 +27,15 @@ namespace beam {
 
 constexpr int kKIterBytes = 256;    // bytes of one row consumed per K iteration
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
 BEAM_DEV uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// streamed-once weights: non-temporal 16-byte load
+BEAM_DEV uint4 ld16_nt(const uint8_t* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // ---------------------------------------------------------------- items
 
@@ -91,8 +101,9 @@ BEAM_DEV void gemm_item(const GemmParams& p, int e, int row0, int rows, int tile
     const int a0 = G1 ? tile * 64 + wave * 16 : tile * 128 + wave * 32;
     const int a1 = G1 ? p.F + a0 : a0 + 16;
     const uint8_t* We = p.W + (size_t)e * nrows_w * kbytes;
-    const uint8_t* pa0 = We + (size_t)(a0 + r) * kbytes + 64 * g;
-    const uint8_t* pa1 = We + (size_t)(a1 + r) * kbytes + 64 * g;
+    // packed tiles: row block a/16 starts at (a/16)*16*kbytes; lane's piece at +lane*16
+    const uint8_t* pa0 = We + (size_t)(a0 >> 4) * 16 * kbytes + lane * 16;
+    const uint8_t* pa1 = We + (size_t)(a1 >> 4) * 16 * kbytes + lane * 16;
 
     const uint8_t* pb[NB];
     bool bval[NB];
@@ -103,10 +114,10 @@ BEAM_DEV void gemm_item(const GemmParams& p, int e, int row0, int rows, int tile
         bval[nb] = c < rows;
         if constexpr (G1) {
             tok[nb] = bval[nb] ? p.row_token[row0 + c] : 0;
-            pb[nb] = p.act + (size_t)tok[nb] * kbytes + 64 * g;
+            pb[nb] = p.act + (size_t)tok[nb] * kbytes + 16 * g;
         } else {
             tok[nb] = row0 + c;
-            pb[nb] = p.act + (size_t)(bval[nb] ? row0 + c : row0) * kbytes + 64 * g;
+            pb[nb] = p.act + (size_t)(bval[nb] ? row0 + c : row0) * kbytes + 16 * g;
         }
     }
 
@@ -119,16 +130,17 @@ BEAM_DEV void gemm_item(const GemmParams& p, int e, int row0, int rows, int tile
 
     uint4 wa0[2][4], wa1[2][4], xb[2][NB][4];
     auto load = [&](int buf, int k) {
+        // k: byte offset along the row, a multiple of 256 (one packed tile)
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            wa0[buf][s] = ld16(pa0 + k + 16 * s);
-            wa1[buf][s] = ld16(pa1 + k + 16 * s);
+            wa0[buf][s] = ld16_nt(pa0 + (size_t)k * 16 + 1024 * s);
+            wa1[buf][s] = ld16_nt(pa1 + (size_t)k * 16 + 1024 * s);
         }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int s = 0; s < 4; ++s)
-                xb[buf][nb][s] = bval[nb] ? ld16(pb[nb] + k + 16 * s) : make_uint4(0, 0, 0, 0);
+                xb[buf][nb][s] = bval[nb] ? ld16(pb[nb] + k + 64 * s) : make_uint4(0, 0, 0, 0);
     };
     auto compute = [&](int buf) {
 #pragma unroll

@@ -57,6 +57,10 @@ struct ExpertsArgs {
 size_t experts_ws_bytes(int T, int K, int E, int H, int F, WKind w);
 hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st);
 
+// Reorders `rows` rows of `kb` bytes (rows % 16 == 0, kb % 256 == 0) into
+// the packed tile layout of the expert GEMM.
+hipError_t launch_pack(const void* src, void* dst, size_t rows, int kb, hipStream_t st);
+
 struct CombineArgs {
     int T, K, H;
     const void* y;

@@ -100,7 +100,7 @@ beam_status beam_moe_route(const beam_moe_cfg* cfg, int32_t T,
  *
  *   topk_ids        [T,K] int32 in (values in [0,E); pair p = t*K + k)
  *   expert_offsets  [E+1] int32 out: exclusive prefix sum of per-expert
- *                   pair counts (expert_offsets[E] = T*K)
+ *                   pair counts (expert_offsets[E] = T*K when every id is valid)
  *   row_token       [T*K] int32 out: permuted row r -> token t
  *   pair_row        [T*K] int32 out: pair p -> permuted row r
  *   Within one expert, rows follow ascending p (stable, unique).
@@ -109,7 +109,9 @@ beam_status beam_moe_route(const beam_moe_cfg* cfg, int32_t T,
  *                   (round to nearest even, saturating at 448)
  *   x_scale         [T] fp32 out (required with x_q): amax(|x[t]|) / 448,
  *                   1 for an all-zero row
- * Ids outside [0,E) are a caller error: they are not checked on the device.
+ * Ids outside [0,E) are a caller error; such pairs are dropped (they get no
+ * row, pair_row is left unwritten for them and expert_offsets[E] counts only
+ * the valid pairs), so no access ever leaves the buffers.
  */
 beam_status beam_moe_permute(const beam_moe_cfg* cfg, int32_t T,
                              const int32_t* topk_ids,
@@ -138,6 +140,8 @@ beam_status beam_moe_permute(const beam_moe_cfg* cfg, int32_t T,
  *   expert_offsets [E+1], row_token [T*K] from beam_moe_permute
  *   w_gate_up [E,2F,H]: rows [0,F) gate, [F,2F) up; s_gate_up [E,2F] iff FP8
  *   w_down    [E,H,F];                               s_down [E,H] iff FP8
+ *             Both weight stacks must be the output of beam_moe_pack_weights
+ *             (same size, tiled layout); the scales stay row-major.
  *   y         [T*K,H] out, dtype y_dtype (F32 or BF16): unweighted expert
  *             outputs in permuted row order
  *   events    nullable array of 4 hipEvent_t recorded on `stream` before
@@ -177,6 +181,27 @@ beam_status beam_moe_combine_norm(const beam_moe_cfg* cfg, int32_t T,
                                   void* h, void* x_next, beam_dtype act_dtype,
                                   const void* gamma_post, const void* gamma_pre,
                                   int32_t n, float* moe_out, void* stream);
+
+/*
+ * beam_moe_pack_weights -- one-time re-layout of expert weight stacks into
+ * the tiled order beam_moe_experts streams from (load time, not per layer
+ * call).  Each expert matrix of R rows x KB bytes is cut into 16-row x
+ * 256-byte tiles stored as [piece s][lane r+16g][16 bytes], lane (r, g)
+ * holding bytes [64s+16g, +16) of row r; the tiles of a 16-row block follow
+ * each other along the row.  Sizes are unchanged.  For F32 stacks the
+ * packed layout is the plain row-major one (a copy).
+ *
+ *   n_experts       number of expert matrices in each stack (may be a
+ *                   subset of cfg->n_experts, to pack expert by expert)
+ *   w_gate_up       [n_experts,2F,H] row-major in; w_down [n_experts,H,F]
+ *   packed_gate_up, packed_down: outputs of the same byte sizes; they must
+ *                   not overlap the inputs or each other.
+ * (Layout choice for MI355X HBM: every weight load instruction of the
+ *  expert GEMM then reads whole 128-byte lines of one contiguous KiB.)
+ */
+beam_status beam_moe_pack_weights(const beam_moe_cfg* cfg, int32_t n_experts, beam_dtype w_dtype,
+                                  const void* w_gate_up, const void* w_down,
+                                  void* packed_gate_up, void* packed_down, void* stream);
 
 /* Workspace bytes that route, permute and experts need for T tokens with
  * experts of w_dtype (the maximum over the three).  0 for invalid input. */

@@ -143,3 +143,18 @@ def test_workspace_bytes(L):
     assert L.beam_moe_workspace_bytes(ctypes.byref(c), 16384, 2) > sizes[-1]
     assert L.beam_moe_workspace_bytes(ctypes.byref(c), -1, 1) == 0
     assert L.beam_moe_workspace_bytes(ctypes.byref(_cfg(hidden=100)), 8, 1) == 0
+
+
+def test_pack_argument_checks(L):
+    c = _cfg()
+    f = lambda n=2, dt=1, a=FAKE, b=FAKE * 1024, pa=FAKE * 4096, pb=FAKE * 8192: L.beam_moe_pack_weights(
+        ctypes.byref(c), n, dt, a, b, pa, pb, None)
+    assert f(n=0) == 0                        # nothing to do
+    assert f(n=-1) == 1
+    assert f(dt=5) == 1
+    assert f(a=None) == 1
+    assert f(pa=FAKE + 8) == 1                # misaligned
+    assert f(pa=FAKE) == 1                    # output overlaps its input
+    assert f(pb=FAKE * 4096 + 4096) == 1      # outputs overlap each other
+    assert L.beam_moe_pack_weights(ctypes.byref(_cfg(d_ff=384)), 1, 2, FAKE, FAKE * 1024, FAKE * 4096,
+                                   FAKE * 8192, None) == 2   # fp8 needs d_ff % 256 == 0

@@ -21,13 +21,14 @@ DEV = "cuda"
 _stacks = {}
 
 
-def stacks(wl):
+def stacks(wl, cfg):
+    """Packed device stacks, generated expert by expert."""
     key = (wl.w_dtype, wl.seed, wl.hidden, wl.d_ff, wl.n_experts)
     if key not in _stacks:
-        say(f"  generating expert stacks {key}")
+        say(f"  generating packed expert stacks {key}")
         _stacks.clear()
         torch.cuda.empty_cache()
-        _stacks[key] = synth.make_expert_stacks(wl, DEV)
+        _stacks[key] = beam.packed_expert_stacks(cfg, lambda e: synth.make_expert(wl, e, DEV), wl.n_experts, DEV)
         torch.cuda.synchronize()
     return _stacks[key]
 
@@ -37,7 +38,7 @@ def run_layer(wname, n_sample):
     say(f"layer {wname}: T={wl.T} w={wl.w_dtype}")
     cfg = beam.LayerCfg(wl.hidden, wl.n_experts, wl.n_groups, wl.topk_groups, wl.topk,
                         wl.group_topn, wl.d_ff, wl.routed_scale, wl.rms_eps)
-    wgu, wd, sgu, sd = stacks(wl)
+    wgu, wd, sgu, sd = stacks(wl, cfg)
     w_r, bias = synth.make_router(wl, DEV)
     x, h, gp, gq = synth.make_activations(wl, DEV)
     fp8 = wl.w_dtype == "fp8"
@@ -75,11 +76,12 @@ def run_layer(wname, n_sample):
             assert s_gpu[t] == s and np.array_equal(q_gpu[t], q), t
 
     tokens = [t for t in sample_tokens(wl.T, n_sample, seed=2) if t not in differ]
-    if fp8:
-        ew = lambda e: {"q_gu": wgu[e].cpu().numpy(), "s_gu": synth.to_f64(sgu[e]),
-                        "q_d": wd[e].cpu().numpy(), "s_d": synth.to_f64(sd[e])}
-    else:
-        ew = lambda e: {"w_gu": synth.to_f64(wgu[e]), "w_d": synth.to_f64(wd[e])}
+    # the oracle reads the plain row-major weights, regenerated per expert
+    def ew(e):
+        a, b, c, d = synth.make_expert(wl, e, DEV)
+        if fp8:
+            return {"q_gu": a.cpu().numpy(), "s_gu": synth.to_f64(c), "q_d": b.cpu().numpy(), "s_d": synth.to_f64(d)}
+        return {"w_gu": synth.to_f64(a), "w_d": synth.to_f64(b)}
     rnd = oracle.round_f32 if wl.act_dtype == "f32" else oracle.round_bf16
     ref = oracle.layer_tokens(ocfg, xn, synth.to_f64(w_r), synth.to_f64(bias), ew, synth.to_f64(h),
                               synth.to_f64(gp), synth.to_f64(gq), wl.n, tokens=tokens,

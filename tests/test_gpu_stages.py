@@ -157,6 +157,8 @@ def _run_experts_stage(wl, T, ids_np, y_dtype):
     cfg = lcfg(wl)
     E, K = wl.n_experts, wl.topk
     wgu, wd, sgu, sd = synth.make_expert_stacks(wl, DEV)
+    pgu, pd = torch.empty_like(wgu), torch.empty_like(wd)
+    beam.beam_moe_pack_weights(cfg, wgu, wd, pgu, pd)
     x, _, _, _ = synth.make_activations(wl, DEV, T=T)
     o_off, o_rt, _ = oracle.permutation(ids_np, E)
     off = torch.from_numpy(o_off.astype(np.int32)).to(DEV)
@@ -169,9 +171,9 @@ def _run_experts_stage(wl, T, ids_np, y_dtype):
         ids = torch.from_numpy(ids_np.astype(np.int32)).to(DEV)
         tmp = [torch.empty(n, dtype=torch.int32, device=DEV) for n in (E + 1, T * K, T * K)]
         beam.beam_moe_permute(cfg, ids, *tmp, x=x, x_q=xq, x_scale=xs, ws=ws)
-        beam.beam_moe_experts(cfg, T, xq, off, rt, wgu, wd, y, x_scale=xs, s_gate_up=sgu, s_down=sd, ws=ws)
+        beam.beam_moe_experts(cfg, T, xq, off, rt, pgu, pd, y, x_scale=xs, s_gate_up=sgu, s_down=sd, ws=ws)
     else:
-        beam.beam_moe_experts(cfg, T, x, off, rt, wgu, wd, y, ws=ws)
+        beam.beam_moe_experts(cfg, T, x, off, rt, pgu, pd, y, ws=ws)
     torch.cuda.synchronize()
     got = y.cpu().double().numpy()
     xn = synth.to_f64(x)
@@ -233,6 +235,29 @@ def test_experts_beam_shape_few_tokens():
     ids = np.array([[0, 1, 2, 3], [3, 4, 5, 6], [7, 0, 3, 5]])
     got, ref = _run_experts_stage(small, 3, ids, torch.float32)
     check_output("y", got, ref, "bf16")
+
+
+@pytest.mark.parametrize("w_dtype", ["bf16", "fp8", "f32"])
+def test_pack_layout(w_dtype):
+    # packed tile (row block rb, 256-byte chunk c) = [piece s][lane r+16g][16 B]
+    # holding bytes [256c + 64s + 16g, +16) of row 16rb + r
+    say(f"pack layout {w_dtype}")
+    wl = _stage_wl(w_dtype, H=512 if w_dtype != "f32" else 256, F=256 if w_dtype != "f32" else 128, E=4)
+    cfg = lcfg(wl)
+    wgu, wd, _, _ = synth.make_expert_stacks(wl, DEV)
+    pgu, pd = torch.empty_like(wgu), torch.empty_like(wd)
+    beam.beam_moe_pack_weights(cfg, wgu, wd, pgu, pd)
+    torch.cuda.synchronize()
+    for src, dst in ((wgu, pgu), (wd, pd)):
+        a = src.cpu().contiguous().view(torch.uint8).numpy().reshape(src.shape[0], src.shape[1], -1)
+        b = dst.cpu().contiguous().view(torch.uint8).numpy().reshape(-1)
+        if w_dtype == "f32":
+            assert np.array_equal(a.reshape(-1), b)
+            continue
+        E, R, KB = a.shape
+        ref = a.reshape(E, R // 16, 16, KB // 256, 4, 4, 16)          # e, rb, r, c, s, g, byte
+        ref = ref.transpose(0, 1, 3, 4, 5, 2, 6).reshape(-1)          # e, rb, c, s, g, r, byte
+        assert np.array_equal(ref, b)
 
 
 # ------------------------------------------------------------------ combine + norm
