@@ -91,44 +91,108 @@ struct GemmParams {
     bool out_bf16;             // G2 only
 };
 
-template <int KIND, bool G1, int NB>
-BEAM_DEV void gemm_item(const GemmParams& p, int e, int row0, int rows, int tile) {
-    constexpr int ES = (KIND == W_BF16) ? 2 : 1;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int r = lane & 15, g = lane >> 4;
-    const int kbytes = (G1 ? p.H : p.F) * ES;
-    const int nrows_w = G1 ? 2 * p.F : p.H;
-    const int a0 = G1 ? tile * 64 + wave * 16 : tile * 128 + wave * 32;
-    const int a1 = G1 ? p.F + a0 : a0 + 16;
-    const uint8_t* We = p.W + (size_t)e * nrows_w * kbytes;
-    // packed tiles: row block a/16 starts at (a/16)*16*kbytes; lane's piece at +lane*16
-    const uint8_t* pa0 = We + (size_t)(a0 >> 4) * 16 * kbytes + lane * 16;
-    const uint8_t* pa1 = We + (size_t)(a1 >> 4) * 16 * kbytes + lane * 16;
+template <int V> struct IC { static constexpr int value = V; };
 
-    const uint8_t* pb[NB];
-    bool bval[NB];
-    int tok[NB];
+// Epilogue for one 16-column block: lane holds D[4g+i][r] = weight row
+// (a0/a1 + 4g + i) x item row `row`.  GEMM1 applies SwiGLU (and the fp8
+// scales) and writes a; GEMM2 writes y.
+template <int KIND, bool G1>
+BEAM_DEV void store_block(const GemmParams& p, int e, int a0, int a1, size_t row, int tok,
+                          const f32x4& acc0, const f32x4& acc1) {
+    const int g = (threadIdx.x & 63) >> 4;
+    const int nrows_w = G1 ? 2 * p.F : p.H;
+    if constexpr (G1) {
+        const int f = a0 + 4 * g;
+        float gv[4], uv[4];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const int c = nb * 16 + r;
-        bval[nb] = c < rows;
-        if constexpr (G1) {
-            tok[nb] = bval[nb] ? p.row_token[row0 + c] : 0;
-            pb[nb] = p.act + (size_t)tok[nb] * kbytes + 16 * g;
+        for (int i = 0; i < 4; ++i) { gv[i] = acc0[i]; uv[i] = acc1[i]; }
+        if constexpr (KIND == W_FP8) {
+            const float sx = p.act_scale[tok];
+            const float4 sg = *reinterpret_cast<const float4*>(p.wscale + (size_t)e * nrows_w + f);
+            const float4 su = *reinterpret_cast<const float4*>(p.wscale + (size_t)e * nrows_w + p.F + f);
+            gv[0] *= sx * sg.x; gv[1] *= sx * sg.y; gv[2] *= sx * sg.z; gv[3] *= sx * sg.w;
+            uv[0] *= sx * su.x; uv[1] *= sx * su.y; uv[2] *= sx * su.z; uv[3] *= sx * su.w;
+            float4 av;
+            av.x = silu_f32(gv[0]) * uv[0];
+            av.y = silu_f32(gv[1]) * uv[1];
+            av.z = silu_f32(gv[2]) * uv[2];
+            av.w = silu_f32(gv[3]) * uv[3];
+            *reinterpret_cast<float4*>(static_cast<float*>(p.out) + row * p.F + f) = av;
         } else {
-            tok[nb] = row0 + c;
-            pb[nb] = p.act + (size_t)(bval[nb] ? row0 + c : row0) * kbytes + 16 * g;
+            uint16_t hb[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16(silu_f32(gv[i]) * uv[i]);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + row * p.F + f) =
+                make_uint2(hb[0] | (uint32_t(hb[1]) << 16), hb[2] | (uint32_t(hb[3]) << 16));
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int o = (t == 0 ? a0 : a1) + 4 * g;
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = (t == 0 ? acc0[i] : acc1[i]);
+            if constexpr (KIND == W_FP8) {
+                const float sa = p.act_scale[row];
+                const float4 sw = *reinterpret_cast<const float4*>(p.wscale + (size_t)e * nrows_w + o);
+                v[0] *= sa * sw.x; v[1] *= sa * sw.y; v[2] *= sa * sw.z; v[3] *= sa * sw.w;
+            }
+            if (p.out_bf16) {
+                uint16_t hb[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16(v[i]);
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + row * p.H + o) =
+                    make_uint2(hb[0] | (uint32_t(hb[1]) << 16), hb[2] | (uint32_t(hb[3]) << 16));
+            } else {
+                *reinterpret_cast<float4*>(static_cast<float*>(p.out) + row * p.H + o) =
+                    make_float4(v[0], v[1], v[2], v[3]);
+            }
         }
     }
+}
 
-    f32x4 acc0[NB], acc1[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        acc0[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        acc1[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+// Weight rows of this wave: GEMM1 16 gate rows + the matching 16 up rows of
+// N-tile `tile` (64 + 64 rows per workgroup); GEMM2 32 output rows (128 per
+// workgroup).  Returns the packed-tile base pointers of the lane's pieces.
+template <int KIND, bool G1>
+BEAM_DEV void weight_rows(const GemmParams& p, int e, int tile, int& a0, int& a1, const uint8_t*& pa0,
+                          const uint8_t*& pa1) {
+    constexpr int ES = (KIND == W_BF16) ? 2 : 1;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kbytes = (G1 ? p.H : p.F) * ES;
+    const int nrows_w = G1 ? 2 * p.F : p.H;
+    a0 = G1 ? tile * 64 + wave * 16 : tile * 128 + wave * 32;
+    a1 = G1 ? p.F + a0 : a0 + 16;
+    const uint8_t* We = p.W + (size_t)e * nrows_w * kbytes;
+    // packed tiles: row block a/16 starts at (a/16)*16*kbytes; lane's piece at +lane*16
+    pa0 = We + (size_t)(a0 >> 4) * 16 * kbytes + lane * 16;
+    pa1 = We + (size_t)(a1 >> 4) * 16 * kbytes + lane * 16;
+}
+
+// ---- small items (<= 16 rows): B fragments straight from L2 into registers
+template <int KIND, bool G1>
+BEAM_DEV void gemm_item_direct(const GemmParams& p, int e, int row0, int rows, int tile) {
+    constexpr int ES = (KIND == W_BF16) ? 2 : 1;
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int kbytes = (G1 ? p.H : p.F) * ES;
+    int a0, a1;
+    const uint8_t *pa0, *pa1;
+    weight_rows<KIND, G1>(p, e, tile, a0, a1, pa0, pa1);
+
+    const bool bval = r < rows;
+    int tok;
+    const uint8_t* pb;
+    if constexpr (G1) {
+        tok = bval ? p.row_token[row0 + r] : 0;
+        pb = p.act + (size_t)tok * kbytes + 16 * g;
+    } else {
+        tok = row0 + r;
+        pb = p.act + (size_t)(bval ? row0 + r : row0) * kbytes + 16 * g;
     }
 
-    uint4 wa0[2][4], wa1[2][4], xb[2][NB][4];
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    uint4 wa0[2][4], wa1[2][4], xb[2][4];
     auto load = [&](int buf, int k) {
         // k: byte offset along the row, a multiple of 256 (one packed tile)
 #pragma unroll
@@ -137,17 +201,11 @@ BEAM_DEV void gemm_item(const GemmParams& p, int e, int row0, int rows, int tile
             wa1[buf][s] = ld16_nt(pa1 + (size_t)k * 16 + 1024 * s);
         }
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                xb[buf][nb][s] = bval[nb] ? ld16(pb[nb] + k + 64 * s) : make_uint4(0, 0, 0, 0);
+        for (int s = 0; s < 4; ++s) xb[buf][s] = bval ? ld16(pb + k + 64 * s) : make_uint4(0, 0, 0, 0);
     };
     auto compute = [&](int buf) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            mfma_kiter<KIND>(wa0[buf], xb[buf][nb], acc0[nb]);
-            mfma_kiter<KIND>(wa1[buf], xb[buf][nb], acc1[nb]);
-        }
+        mfma_kiter<KIND>(wa0[buf], xb[buf], acc0);
+        mfma_kiter<KIND>(wa1[buf], xb[buf], acc1);
     };
 
     load(0, 0);
@@ -158,79 +216,131 @@ BEAM_DEV void gemm_item(const GemmParams& p, int e, int row0, int rows, int tile
         if (k + 2 * kKIterBytes < kbytes) load(0, k + 2 * kKIterBytes);
         if (has1) compute(1);
     }
+    if (bval) store_block<KIND, G1>(p, e, a0, a1, (size_t)row0 + r, tok, acc0, acc1);
+}
 
-    // epilogue: lane holds D[4g+i][r] = output row (a0/a1 + 4g + i) x item row (nb*16 + r)
+// ---- large items (<= kLdsRows rows): the item's activation rows are staged
+// once per workgroup in LDS (double-buffered, 256 bytes of K per stage) and
+// shared by the 4 waves; weights keep streaming into registers.
+constexpr int kLdsRows = 128;
+
+// LDS position of 16-byte chunk c of staged row rr: chunks are XOR-swizzled
+// with the row's low 4 bits so the 16 rows read by one MFMA fragment load
+// hit 16 different bank groups.
+BEAM_DEV int lds_pos(int rr, int c) { return rr * 16 + (c ^ (rr & 15)); }
+
+template <int KIND, bool G1, int NB>
+BEAM_DEV void gemm_item_lds(const GemmParams& p, int e, int row0, int rows, int tile,
+                            uint4 (*bs)[kLdsRows * 16]) {
+    constexpr int ES = (KIND == W_BF16) ? 2 : 1;
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int kbytes = (G1 ? p.H : p.F) * ES;
+    const int nk = kbytes / kKIterBytes;
+    int a0, a1;
+    const uint8_t *pa0, *pa1;
+    weight_rows<KIND, G1>(p, e, tile, a0, a1, pa0, pa1);
+
+    // loader role: thread t copies chunk c = t % 16 of rows t/16 + 16 i
+    const int lc = threadIdx.x & 15, lr = threadIdx.x >> 4;
+    const uint8_t* src[NB];
+    bool sval[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const int rr = lr + 16 * i;
+        sval[i] = rr < rows;
+        size_t srow = row0;
+        if (sval[i]) srow = G1 ? (size_t)p.row_token[row0 + rr] : (size_t)(row0 + rr);
+        else if (G1) srow = 0;
+        src[i] = p.act + srow * kbytes + 16 * lc;
+    }
+    uint4 stage[NB];
+    auto gload = [&](int k) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) stage[i] = sval[i] ? ld16(src[i] + k) : make_uint4(0, 0, 0, 0);
+    };
+    auto swrite = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) bs[buf][lds_pos(lr + 16 * i, lc)] = stage[i];
+    };
+
+    f32x4 acc0[NB], acc1[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-        if (!bval[nb]) continue;
-        const size_t row = (size_t)row0 + nb * 16 + r;
-        if constexpr (G1) {
-            const int f = a0 + 4 * g;
-            float gv[4], uv[4];
+        acc0[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc1[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    uint4 wa0[2][4], wa1[2][4];
+    auto aload = [&](int buf, int k) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) { gv[i] = acc0[nb][i]; uv[i] = acc1[nb][i]; }
-            if constexpr (KIND == W_FP8) {
-                const float sx = p.act_scale[tok[nb]];
-                const float4 sg = *reinterpret_cast<const float4*>(p.wscale + (size_t)e * nrows_w + f);
-                const float4 su = *reinterpret_cast<const float4*>(p.wscale + (size_t)e * nrows_w + p.F + f);
-                gv[0] *= sx * sg.x; gv[1] *= sx * sg.y; gv[2] *= sx * sg.z; gv[3] *= sx * sg.w;
-                uv[0] *= sx * su.x; uv[1] *= sx * su.y; uv[2] *= sx * su.z; uv[3] *= sx * su.w;
-                float4 av;
-                av.x = silu_f32(gv[0]) * uv[0];
-                av.y = silu_f32(gv[1]) * uv[1];
-                av.z = silu_f32(gv[2]) * uv[2];
-                av.w = silu_f32(gv[3]) * uv[3];
-                *reinterpret_cast<float4*>(static_cast<float*>(p.out) + row * p.F + f) = av;
-            } else {
-                uint16_t hb[4];
+        for (int s = 0; s < 4; ++s) {
+            wa0[buf][s] = ld16_nt(pa0 + (size_t)k * 16 + 1024 * s);
+            wa1[buf][s] = ld16_nt(pa1 + (size_t)k * 16 + 1024 * s);
+        }
+    };
+    // one K step on LDS buffer CUR; prefetches step kit+1 into the other buffer
+    auto step = [&](auto curc, int kit) {
+        constexpr int CUR = decltype(curc)::value;
+        const bool more = kit + 1 < nk;
+        if (more) {
+            gload((kit + 1) * kKIterBytes);
+            aload(CUR ^ 1, (kit + 1) * kKIterBytes);
+        }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16(silu_f32(gv[i]) * uv[i]);
-                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + row * p.F + f) =
-                    make_uint2(hb[0] | (uint32_t(hb[1]) << 16), hb[2] | (uint32_t(hb[3]) << 16));
-            }
-        } else {
+        for (int nb = 0; nb < NB; ++nb) {
+            uint4 xb[4];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int o = (t == 0 ? a0 : a1) + 4 * g;
-                float v[4];
+            for (int s = 0; s < 4; ++s) xb[s] = bs[CUR][lds_pos(nb * 16 + r, 4 * s + g)];
+            mfma_kiter<KIND>(wa0[CUR], xb, acc0[nb]);
+            mfma_kiter<KIND>(wa1[CUR], xb, acc1[nb]);
+        }
+        if (more) swrite(CUR ^ 1);
+        __syncthreads();
+    };
+
+    gload(0);
+    aload(0, 0);
+    swrite(0);
+    __syncthreads();
+    for (int kit = 0; kit < nk; kit += 2) {
+        step(IC<0>{}, kit);
+        if (kit + 1 < nk) step(IC<1>{}, kit + 1);
+    }
+
 #pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = (t == 0 ? acc0[nb][i] : acc1[nb][i]);
-                if constexpr (KIND == W_FP8) {
-                    const float sa = p.act_scale[row];
-                    const float4 sw = *reinterpret_cast<const float4*>(p.wscale + (size_t)e * nrows_w + o);
-                    v[0] *= sa * sw.x; v[1] *= sa * sw.y; v[2] *= sa * sw.z; v[3] *= sa * sw.w;
-                }
-                if (p.out_bf16) {
-                    uint16_t hb[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16(v[i]);
-                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + row * p.H + o) =
-                        make_uint2(hb[0] | (uint32_t(hb[1]) << 16), hb[2] | (uint32_t(hb[3]) << 16));
-                } else {
-                    *reinterpret_cast<float4*>(static_cast<float*>(p.out) + row * p.H + o) =
-                        make_float4(v[0], v[1], v[2], v[3]);
-                }
-            }
+    for (int nb = 0; nb < NB; ++nb) {
+        const int c = nb * 16 + r;
+        if (c < rows) {
+            const int tok = G1 ? p.row_token[row0 + c] : row0 + c;
+            store_block<KIND, G1>(p, e, a0, a1, (size_t)row0 + c, tok, acc0[nb], acc1[nb]);
         }
     }
 }
 
-template <int KIND, bool G1, int NBMAX>
-__global__ __launch_bounds__(256) void beam_expert_gemm(GemmParams p) {
+template <int KIND, bool G1>
+__global__ __launch_bounds__(256) void beam_expert_gemm_direct(GemmParams p) {
     const int item = blockIdx.x / p.n_tiles;
     const int tile = blockIdx.x - item * p.n_tiles;
     if (item >= *p.n_items) return;
     const int4 it = p.items[item];
-    if constexpr (NBMAX == 1) {
-        gemm_item<KIND, G1, 1>(p, it.x, it.y, it.z, tile);
-    } else {
-        if (it.z <= 16)
-            gemm_item<KIND, G1, 1>(p, it.x, it.y, it.z, tile);
-        else if (it.z <= 32)
-            gemm_item<KIND, G1, 2>(p, it.x, it.y, it.z, tile);
-        else
-            gemm_item<KIND, G1, 4>(p, it.x, it.y, it.z, tile);
-    }
+    gemm_item_direct<KIND, G1>(p, it.x, it.y, it.z, tile);
+}
+
+template <int KIND, bool G1>
+__global__ __launch_bounds__(256) void beam_expert_gemm_lds(GemmParams p) {
+    __shared__ uint4 bs[2][kLdsRows * 16];
+    const int item = blockIdx.x / p.n_tiles;
+    const int tile = blockIdx.x - item * p.n_tiles;
+    if (item >= *p.n_items) return;
+    const int4 it = p.items[item];
+    if (it.z <= 16)
+        gemm_item_lds<KIND, G1, 1>(p, it.x, it.y, it.z, tile, bs);
+    else if (it.z <= 32)
+        gemm_item_lds<KIND, G1, 2>(p, it.x, it.y, it.z, tile, bs);
+    else if (it.z <= 64)
+        gemm_item_lds<KIND, G1, 4>(p, it.x, it.y, it.z, tile, bs);
+    else
+        gemm_item_lds<KIND, G1, 8>(p, it.x, it.y, it.z, tile, bs);
 }
 
 // Per-row e4m3 re-quantisation of the fp32 SwiGLU output (fp8 path).
@@ -299,7 +409,10 @@ __global__ __launch_bounds__(256) void beam_expert_f32_gemm2(
 
 static size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-static int rows_per_item(int T) { return T <= 16 ? 16 : 64; }
+// Decode-sized batches use 16-row items (every touched expert is one item,
+// so weights are read exactly once); larger batches use 128-row items whose
+// activations are shared through LDS.
+static int rows_per_item(int T) { return T <= 16 ? 16 : kLdsRows; }
 
 static size_t max_items(int T, int K, int E) {
     const size_t TK = (size_t)T * K;
@@ -342,11 +455,11 @@ size_t experts_ws_bytes(int T, int K, int E, int H, int F, WKind w) {
 }
 
 template <int KIND, bool G1>
-static void launch_gemm(const GemmParams& p, int n_blocks, int nbmax, hipStream_t st) {
-    if (nbmax == 1)
-        hipLaunchKernelGGL((beam_expert_gemm<KIND, G1, 1>), dim3(n_blocks), dim3(256), 0, st, p);
+static void launch_gemm(const GemmParams& p, int n_blocks, int mc, hipStream_t st) {
+    if (mc == 16)
+        hipLaunchKernelGGL((beam_expert_gemm_direct<KIND, G1>), dim3(n_blocks), dim3(256), 0, st, p);
     else
-        hipLaunchKernelGGL((beam_expert_gemm<KIND, G1, 4>), dim3(n_blocks), dim3(256), 0, st, p);
+        hipLaunchKernelGGL((beam_expert_gemm_lds<KIND, G1>), dim3(n_blocks), dim3(256), 0, st, p);
 }
 
 static void record(hipEvent_t ev, hipStream_t st) {
@@ -368,7 +481,6 @@ hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st) {
         return hipGetLastError();
     }
     const int mc = rows_per_item(a.T);
-    const int nbmax = mc / 16;
     const int n_items_max = (int)max_items(a.T, a.K, a.E);
     hipLaunchKernelGGL(beam_build_items, dim3(1), dim3(256), 0, st, a.offsets, a.E, mc, ws.items,
                        ws.n_items);
@@ -390,9 +502,9 @@ hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st) {
     p.out_bf16 = false;
     record(a.ev[0], st);
     if (a.w == W_BF16)
-        launch_gemm<W_BF16, true>(p, n_items_max * p.n_tiles, nbmax, st);
+        launch_gemm<W_BF16, true>(p, n_items_max * p.n_tiles, mc, st);
     else
-        launch_gemm<W_FP8, true>(p, n_items_max * p.n_tiles, nbmax, st);
+        launch_gemm<W_FP8, true>(p, n_items_max * p.n_tiles, mc, st);
     record(a.ev[1], st);
 
     // GEMM2
@@ -408,12 +520,12 @@ hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st) {
         p.act = ws.aq;
         p.act_scale = ws.ascale;
         record(a.ev[2], st);
-        launch_gemm<W_FP8, false>(p, n_items_max * p.n_tiles, nbmax, st);
+        launch_gemm<W_FP8, false>(p, n_items_max * p.n_tiles, mc, st);
     } else {
         p.act = static_cast<const uint8_t*>(ws.a);
         p.act_scale = nullptr;
         record(a.ev[2], st);
-        launch_gemm<W_BF16, false>(p, n_items_max * p.n_tiles, nbmax, st);
+        launch_gemm<W_BF16, false>(p, n_items_max * p.n_tiles, mc, st);
     }
     record(a.ev[3], st);
     return hipGetLastError();
