@@ -41,7 +41,9 @@ bool valid_dtype(beam_dtype d) { return d == BEAM_F32 || d == BEAM_BF16 || d == 
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-size_t route_ws(const beam_moe_cfg* c, int T) { return align256((size_t)T * c->n_experts * sizeof(float)); }
+size_t route_ws(const beam_moe_cfg* c, int T) {
+    return align256(beam::route_partials_bytes(T, c->hidden, c->n_experts));
+}
 
 beam::WKind wkind(beam_dtype d) {
     return d == BEAM_BF16 ? beam::W_BF16 : (d == BEAM_FP8_E4M3 ? beam::W_FP8 : beam::W_F32);
@@ -86,11 +88,7 @@ beam_status beam_moe_route(const beam_moe_cfg* cfg, int32_t T, const void* x, be
     if (!x || !w_router || !bias || !topk_ids || !topk_w) return BEAM_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(w_router) || (logits_out && !aligned16(logits_out)))
         return BEAM_ERR_INVALID_ARG;
-    float* logits = logits_out;
-    if (!logits) {
-        if (!ws || ws_bytes < route_ws(cfg, T)) return BEAM_ERR_WORKSPACE;
-        logits = static_cast<float*>(ws);
-    }
+    if (!ws || ws_bytes < route_ws(cfg, T) || !aligned16(ws)) return BEAM_ERR_WORKSPACE;
     beam::RouteArgs a{};
     a.T = T;
     a.H = cfg->hidden;
@@ -104,7 +102,8 @@ beam_status beam_moe_route(const beam_moe_cfg* cfg, int32_t T, const void* x, be
     a.x_bf16 = x_dtype == BEAM_BF16;
     a.w = w_router;
     a.bias = bias;
-    a.logits = logits;
+    a.logits_out = logits_out;
+    a.partials = static_cast<float*>(ws);
     a.ids = topk_ids;
     a.wts = topk_w;
     return beam::launch_route(a, static_cast<hipStream_t>(stream)) == hipSuccess ? BEAM_OK

@@ -15,12 +15,14 @@ struct RouteArgs {
     bool x_bf16;
     const float* w;
     const float* bias;
-    float* logits;      // [T,E] (caller's logits_out or workspace)
+    float* logits_out;  // [T,E] or null
+    float* partials;    // workspace, route_partials_bytes(T, H, E)
     int32_t* ids;
     float* wts;
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t st);
 int route_epl(int E);
+size_t route_partials_bytes(int T, int H, int E);
 
 struct PermuteArgs {
     int T, K, E, H;

@@ -156,6 +156,107 @@ __global__ __launch_bounds__(256) void beam_router_logits_tiled(
 }
 
 // ---------------------------------------------------------------------------
+// Batched logits on matrix cores.  The fp32 router weights are split on the
+// fly into three bf16 planes, W = hi + mid + lo, each plane holding the next
+// 8 significant bits (the split is exact: every residual is representable),
+// so every product x*hi, x*mid, x*lo of a bf16 activation is exact in fp32
+// and the bf16 MFMA accumulates them in fp32 -- the pages' exact three-way
+// bf16 decomposition of the FP32 router for large batches.
+// Workgroup tile: 64 tokens x 64 experts; each wave owns 16 experts and all
+// four 16-token blocks.  K is split over gridDim.z slices (deterministic
+// partial sums, added in slice order by the selection kernel) so small
+// batches still fill the chip.  Operands are staged through LDS (rows
+// padded to 80 bytes: conflict-free 16-byte fragment reads), double-buffered
+// in steps of 32 along K.
+// ---------------------------------------------------------------------------
+constexpr int kMT = 64, kME = 64, kMK = 32;
+
+BEAM_DEV void split3_bf16(float v, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t h = u & 0xFFFF0000u;                 // top 8 significant bits
+    const float r1 = v - __uint_as_float(h);            // exact
+    const uint32_t m = __float_as_uint(r1) & 0xFFFF0000u;
+    const float r2 = r1 - __uint_as_float(m);           // exact, <= 8 significant bits
+    hi = h >> 16;
+    mid = m >> 16;
+    lo = __float_as_uint(r2) >> 16;
+}
+
+__global__ __launch_bounds__(256) void beam_router_logits_mfma(
+    const uint16_t* __restrict__ x, const float* __restrict__ w, float* __restrict__ part,
+    int T, int H, int E, int kchunk) {
+    __shared__ uint4 xs[2][kMT][5];
+    __shared__ uint4 wsh[2][3][kME][5];
+    const int t0 = blockIdx.x * kMT, e0 = blockIdx.y * kME, sl = blockIdx.z;
+    const int kbeg = sl * kchunk, nk = kchunk / kMK;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    // loader role: row lr (token / expert of the tile), 8-element chunk lc
+    const int lr = tid >> 2, lc = tid & 3;
+    const bool tv = t0 + lr < T;
+    const uint16_t* xp = x + (size_t)(tv ? t0 + lr : 0) * H + kbeg + 8 * lc;
+    const float* wp = w + (size_t)(e0 + lr) * H + kbeg + 8 * lc;
+    uint4 xr;
+    float4 w0, w1;
+    auto gload = [&](int kk) {
+        xr = tv ? *reinterpret_cast<const uint4*>(xp + kk) : make_uint4(0, 0, 0, 0);
+        w0 = *reinterpret_cast<const float4*>(wp + kk);
+        w1 = *reinterpret_cast<const float4*>(wp + kk + 4);
+    };
+    auto swrite = [&](int buf) {
+        xs[buf][lr][lc] = xr;
+        const float v[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        uint32_t hp[4], mp[4], lp[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t h0, m0, l0, h1, m1, l1;
+            split3_bf16(v[2 * j], h0, m0, l0);
+            split3_bf16(v[2 * j + 1], h1, m1, l1);
+            hp[j] = h0 | (h1 << 16);
+            mp[j] = m0 | (m1 << 16);
+            lp[j] = l0 | (l1 << 16);
+        }
+        wsh[buf][0][lr][lc] = make_uint4(hp[0], hp[1], hp[2], hp[3]);
+        wsh[buf][1][lr][lc] = make_uint4(mp[0], mp[1], mp[2], mp[3]);
+        wsh[buf][2][lr][lc] = make_uint4(lp[0], lp[1], lp[2], lp[3]);
+    };
+
+    f32x4 acc[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    gload(0);
+    swrite(0);
+    __syncthreads();
+    for (int it = 0; it < nk; ++it) {
+        const int cur = it & 1;
+        const bool more = it + 1 < nk;
+        if (more) gload((it + 1) * kMK);
+        bf16x8 a[3];
+#pragma unroll
+        for (int pl = 0; pl < 3; ++pl) a[pl] = __builtin_bit_cast(bf16x8, wsh[cur][pl][wave * 16 + r][g]);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const bf16x8 b = __builtin_bit_cast(bf16x8, xs[cur][nb * 16 + r][g]);
+            // small terms first
+            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], b, acc[nb], 0, 0, 0);
+            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], b, acc[nb], 0, 0, 0);
+            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b, acc[nb], 0, 0, 0);
+        }
+        if (more) swrite(cur ^ 1);
+        __syncthreads();
+    }
+    // lane holds D[4g+i][r] = expert e0 + 16*wave + 4g + i, token t0 + 16*nb + r
+    float* out = part + (size_t)sl * T * E;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+        const int t = t0 + nb * 16 + r;
+        if (t < T)
+            *reinterpret_cast<float4*>(out + (size_t)t * E + e0 + wave * 16 + 4 * g) =
+                make_float4(acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3]);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Selection: one wave per token.  Lane l holds experts [l*EPL, l*EPL+EPL);
 // a group of E/G experts spans LPG = E/G/EPL consecutive lanes.
 //   s = sigmoid(logit), b = s + bias (fp32)
@@ -170,20 +271,24 @@ constexpr int kMaxTopn = 4;
 
 template <int EPL>
 __global__ __launch_bounds__(256) void beam_route_select(
-    const float* __restrict__ logits, const float* __restrict__ bias,
-    int32_t* __restrict__ ids_out, float* __restrict__ w_out,
+    const float* __restrict__ part, int nsplit, float* __restrict__ logits_out,
+    const float* __restrict__ bias, int32_t* __restrict__ ids_out, float* __restrict__ w_out,
     int T, int E, int G, int kg, int K, int topn, int lpg, float scale) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;   // whole wave exits together
-    const float* lg = logits + (size_t)t * E;
+    const size_t TE = (size_t)T * E;
 
     float s[EPL], b[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = lane * EPL + i;
         if (e < E) {
-            const float z = lg[e];
+            // logits = partial sums over the K slices, added in slice order
+            const size_t at = (size_t)t * E + e;
+            float z = part[at];
+            for (int sl = 1; sl < nsplit; ++sl) z += part[sl * TE + at];
+            if (logits_out && logits_out != part) logits_out[at] = z;
             s[i] = 1.0f / (1.0f + expf(-z));
             b[i] = s[i] + bias[e];
         } else {
@@ -283,23 +388,52 @@ __global__ __launch_bounds__(256) void beam_route_select(
 
 int route_epl(int E) { return E <= 64 ? 1 : (E <= 128 ? 2 : 4); }
 
+
+// K slices of the matrix-core router for T tokens: enough workgroups to
+// fill the chip, each slice a multiple of 32 that divides H, at least 256.
+int route_splits(int T, int H, int E) {
+    if (T <= 0 || E % kME != 0) return 1;   // only the matrix-core router splits K
+    const int tiles = ((T + kMT - 1) / kMT) * (E / kME);
+    int want = (640 + tiles - 1) / tiles;
+    const int steps = H / kMK;
+    if (want > H / 256) want = H / 256;
+    for (int sl = want; sl > 1; --sl)
+        if (steps % sl == 0) return sl;
+    return 1;
+}
+
+bool route_uses_mfma(int T, int E, bool x_bf16) { return T > kSmallT && x_bf16 && E % kME == 0; }
+
+size_t route_partials_bytes(int T, int H, int E) {
+    return (size_t)route_splits(T, H, E) * T * E * sizeof(float);
+}
+
 hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
     const int T = a.T, H = a.H, E = a.E;
+    // partial logits: the caller's logits_out when there is a single slice,
+    // else the workspace
+    int nsplit = 1;
+    if (route_uses_mfma(T, E, a.x_bf16)) nsplit = route_splits(T, H, E);
+    float* part = (nsplit == 1 && a.logits_out) ? a.logits_out : a.partials;
     if (T <= kSmallT) {
         if (a.x_bf16)
             hipLaunchKernelGGL(beam_router_logits_small<uint16_t>, dim3(E), dim3(256), 0, st,
-                               (const uint16_t*)a.x, a.w, a.logits, T, H, E);
+                               (const uint16_t*)a.x, a.w, part, T, H, E);
         else
             hipLaunchKernelGGL(beam_router_logits_small<float>, dim3(E), dim3(256), 0, st,
-                               (const float*)a.x, a.w, a.logits, T, H, E);
+                               (const float*)a.x, a.w, part, T, H, E);
+    } else if (route_uses_mfma(T, E, a.x_bf16)) {
+        dim3 grid((T + kMT - 1) / kMT, E / kME, nsplit);
+        hipLaunchKernelGGL(beam_router_logits_mfma, grid, dim3(256), 0, st, (const uint16_t*)a.x, a.w,
+                           part, T, H, E, H / nsplit);
     } else {
         dim3 grid((T + kLT - 1) / kLT, (E + kLE - 1) / kLE);
         if (a.x_bf16)
             hipLaunchKernelGGL(beam_router_logits_tiled<uint16_t>, grid, dim3(256), 0, st,
-                               (const uint16_t*)a.x, a.w, a.logits, T, H, E);
+                               (const uint16_t*)a.x, a.w, part, T, H, E);
         else
             hipLaunchKernelGGL(beam_router_logits_tiled<float>, grid, dim3(256), 0, st,
-                               (const float*)a.x, a.w, a.logits, T, H, E);
+                               (const float*)a.x, a.w, part, T, H, E);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -308,16 +442,16 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
     dim3 grid((T + 3) / 4);
     switch (epl) {
         case 1:
-            hipLaunchKernelGGL(beam_route_select<1>, grid, dim3(256), 0, st, a.logits, a.bias, a.ids,
-                               a.wts, T, E, a.G, a.kg, a.K, a.topn, lpg, a.scale);
+            hipLaunchKernelGGL(beam_route_select<1>, grid, dim3(256), 0, st, part, nsplit, a.logits_out,
+                               a.bias, a.ids, a.wts, T, E, a.G, a.kg, a.K, a.topn, lpg, a.scale);
             break;
         case 2:
-            hipLaunchKernelGGL(beam_route_select<2>, grid, dim3(256), 0, st, a.logits, a.bias, a.ids,
-                               a.wts, T, E, a.G, a.kg, a.K, a.topn, lpg, a.scale);
+            hipLaunchKernelGGL(beam_route_select<2>, grid, dim3(256), 0, st, part, nsplit, a.logits_out,
+                               a.bias, a.ids, a.wts, T, E, a.G, a.kg, a.K, a.topn, lpg, a.scale);
             break;
         default:
-            hipLaunchKernelGGL(beam_route_select<4>, grid, dim3(256), 0, st, a.logits, a.bias, a.ids,
-                               a.wts, T, E, a.G, a.kg, a.K, a.topn, lpg, a.scale);
+            hipLaunchKernelGGL(beam_route_select<4>, grid, dim3(256), 0, st, part, nsplit, a.logits_out,
+                               a.bias, a.ids, a.wts, T, E, a.G, a.kg, a.K, a.topn, lpg, a.scale);
             break;
     }
     return hipGetLastError();

@@ -83,8 +83,13 @@ typedef struct beam_moe_cfg {
  *   topk_w     [T,K] fp32 out: routed_scale * s_k / sum_j s_j over the K
  *                    chosen experts (s = sigmoid(logit), unbiased)
  *   logits_out [T,E] fp32 out, nullable: the router logits
+ *   ws         required (partial logits), see beam_moe_workspace_bytes
  * Group score = sum of the group_topn largest biased scores of the group;
  * the topk_groups best groups are kept (ties: lower group index).
+ * For T > 16 with bf16 x the logits run on matrix cores through the exact
+ * three-way bf16 split of the fp32 router weights (TokenSpeed blog, "Fused
+ * FP32 routing": Tensor Core path for large batches); products are exact
+ * and accumulation is fp32 in every path.
  */
 beam_status beam_moe_route(const beam_moe_cfg* cfg, int32_t T,
                            const void* x, beam_dtype x_dtype,

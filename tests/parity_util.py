@@ -56,22 +56,31 @@ def check_output(name, got, ref, kind):
 
 
 def _valid_near_tie_choice(ids, r, cfg):
-    """A different selection is valid if every chosen expert lies in a group
-    whose score is within NEAR_TIE of the last kept group score and has a
-    biased score within NEAR_TIE of the oracle's K-th expert."""
-    per = cfg["n_experts"] // cfg["n_groups"]
-    gs_sorted = sorted(r.group_scores, reverse=True)
-    g_last = gs_sorted[cfg["topk_groups"] - 1]
-    b_last = r.biased[r.ids[-1]]
-    if len(set(int(e) for e in ids)) != len(ids):
+    """A different selection is valid if it is the top-K (by the oracle's
+    biased scores, up to experts within NEAR_TIE of the K-th) of some group
+    set that is itself a top-`topk_groups` choice up to groups within
+    NEAR_TIE of the last kept group score."""
+    import itertools
+    G, per = cfg["n_groups"], cfg["n_experts"] // cfg["n_groups"]
+    kg, K = cfg["topk_groups"], cfg["topk"]
+    ids = [int(e) for e in ids]
+    if len(set(ids)) != len(ids) or len(ids) != K:
         return False
-    for e in ids:
-        g = int(e) // per
-        if r.group_scores[g] < g_last - NEAR_TIE * abs(g_last):
-            return False
-        if r.biased[int(e)] < b_last - NEAR_TIE * abs(b_last):
-            return False
-    return True
+    gs = r.group_scores
+    g_last = sorted(gs, reverse=True)[kg - 1]
+    tol_g = NEAR_TIE * abs(g_last)
+    sure_g = [g for g in range(G) if gs[g] > g_last + tol_g]
+    amb_g = [g for g in range(G) if abs(gs[g] - g_last) <= tol_g]
+    for combo in itertools.combinations(amb_g, kg - len(sure_g)):
+        cand = [e for g in sure_g + list(combo) for e in range(g * per, (g + 1) * per)]
+        bs = sorted((r.biased[e] for e in cand), reverse=True)
+        b_k = bs[K - 1]
+        tol_e = NEAR_TIE * abs(b_k)
+        sure_e = {e for e in cand if r.biased[e] > b_k + tol_e}
+        amb_e = {e for e in cand if abs(r.biased[e] - b_k) <= tol_e}
+        if sure_e <= set(ids) and set(ids) - sure_e <= amb_e:
+            return True
+    return False
 
 
 def _order_ok(ids, r):

@@ -143,6 +143,11 @@ def test_workspace_bytes(L):
     assert L.beam_moe_workspace_bytes(ctypes.byref(c), 16384, 2) > sizes[-1]
     assert L.beam_moe_workspace_bytes(ctypes.byref(c), -1, 1) == 0
     assert L.beam_moe_workspace_bytes(ctypes.byref(_cfg(hidden=100)), 8, 1) == 0
+    # small expert counts (no matrix-core router tiles) and every dtype
+    tiny = beam.LayerCfg(256, 16, 4, 2, 4, 2, 128).c()
+    for dt in (0, 1):
+        for T in (1, 4, 17, 33, 1000):
+            assert L.beam_moe_workspace_bytes(ctypes.byref(tiny), T, dt) > 0
 
 
 def test_pack_argument_checks(L):

@@ -29,7 +29,8 @@ def lcfg(wl):
 @pytest.mark.parametrize("wname,T", [
     ("tiny_fp32", 1), ("tiny_fp32", 4), ("tiny_fp32", 33),
     ("decode_t8", 1), ("decode_t8", 8), ("decode_t8", 16), ("decode_t8", 17),
-    ("skew_t64", 64), ("decode_t8", 300), ("prefill_t2048", 2048),
+    ("skew_t64", 64), ("decode_t8", 300), ("prefill_t2048", 2048), ("decode_t8", 100),
+    ("prefill_fp8_t16384", 16384),
 ])
 def test_route_parity(wname, T):
     wl = synth.WORKLOADS[wname]
@@ -40,7 +41,7 @@ def test_route_parity(wname, T):
     ids = torch.empty((T, wl.topk), dtype=torch.int32, device=DEV)
     w = torch.empty((T, wl.topk), dtype=torch.float32, device=DEV)
     logits = torch.empty((T, wl.n_experts), dtype=torch.float32, device=DEV)
-    beam.beam_moe_route(cfg, x, w_r, bias, ids, w, logits)
+    beam.beam_moe_route(cfg, x, w_r, bias, ids, w, logits, ws=beam.workspace(cfg, T, beam.BEAM_BF16))
     torch.cuda.synchronize()
     ref = oracle.router_logits(synth.to_f64(x), synth.to_f64(w_r))
     got = logits.cpu().double().numpy()
@@ -56,8 +57,9 @@ def test_route_parity(wname, T):
     check_routes(ids.cpu().numpy(), w.cpu().numpy(), routes, oracle_cfg(wl))
 
 
-def test_route_without_logits_output_uses_workspace():
-    wl = synth.WORKLOADS["decode_t8"]
+@pytest.mark.parametrize("T", [8, 64, 2048])
+def test_route_without_logits_output_uses_workspace(T):
+    wl = synth.WORKLOADS["decode_t8"].with_T(T)
     cfg = lcfg(wl)
     w_r, bias = synth.make_router(wl, DEV)
     x, _, _, _ = synth.make_activations(wl, DEV)
@@ -65,8 +67,9 @@ def test_route_without_logits_output_uses_workspace():
     w = torch.empty((wl.T, wl.topk), dtype=torch.float32, device=DEV)
     ids2, w2 = torch.empty_like(ids), torch.empty_like(w)
     lg = torch.empty((wl.T, wl.n_experts), dtype=torch.float32, device=DEV)
-    beam.beam_moe_route(cfg, x, w_r, bias, ids, w, lg)
-    beam.beam_moe_route(cfg, x, w_r, bias, ids2, w2, None, ws=beam.workspace(cfg, wl.T, beam.BEAM_BF16))
+    ws = beam.workspace(cfg, wl.T, beam.BEAM_BF16)
+    beam.beam_moe_route(cfg, x, w_r, bias, ids, w, lg, ws=ws)
+    beam.beam_moe_route(cfg, x, w_r, bias, ids2, w2, None, ws=ws)
     torch.cuda.synchronize()
     assert torch.equal(ids, ids2) and torch.equal(w, w2)
 
