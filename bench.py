@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--all", action="store_true", help="also time the other Beam workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=8)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run 3 plain device copies of MIB MiB (counter calibration) and exit")
     return ap.parse_args()
 
 
@@ -233,6 +235,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 3}))
+        return
     import expert_routed_ffn_amd as beam
     import synth
     if not os.path.exists(beam.LIB_PATH):
