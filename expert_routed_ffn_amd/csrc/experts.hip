@@ -55,6 +55,8 @@ __global__ __launch_bounds__(256) void beam_build_items(const int32_t* __restric
 
 // ---------------------------------------------------------------- MFMA
 
+typedef int i32x4v __attribute__((ext_vector_type(4)));
+
 template <int KIND>
 BEAM_DEV void mfma_kiter(const uint4 (&a)[4], const uint4 (&b)[4], f32x4& acc) {
     if constexpr (KIND == W_BF16) {
@@ -65,12 +67,12 @@ BEAM_DEV void mfma_kiter(const uint4 (&a)[4], const uint4 (&b)[4], f32x4& acc) {
     } else {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            const i32x8 av = {(int)a[2 * s].x, (int)a[2 * s].y, (int)a[2 * s].z, (int)a[2 * s].w,
-                              (int)a[2 * s + 1].x, (int)a[2 * s + 1].y, (int)a[2 * s + 1].z,
-                              (int)a[2 * s + 1].w};
-            const i32x8 bv = {(int)b[2 * s].x, (int)b[2 * s].y, (int)b[2 * s].z, (int)b[2 * s].w,
-                              (int)b[2 * s + 1].x, (int)b[2 * s + 1].y, (int)b[2 * s + 1].z,
-                              (int)b[2 * s + 1].w};
+            const i32x8 av = __builtin_shufflevector(__builtin_bit_cast(i32x4v, a[2 * s]),
+                                                     __builtin_bit_cast(i32x4v, a[2 * s + 1]),
+                                                     0, 1, 2, 3, 4, 5, 6, 7);
+            const i32x8 bv = __builtin_shufflevector(__builtin_bit_cast(i32x4v, b[2 * s]),
+                                                     __builtin_bit_cast(i32x4v, b[2 * s + 1]),
+                                                     0, 1, 2, 3, 4, 5, 6, 7);
             // formats 0/0 = e4m3 x e4m3; block scales 127 = 2^0 (unscaled)
             acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 0, 0, 0, 127, 0, 127);
         }
@@ -326,8 +328,11 @@ __global__ __launch_bounds__(256) void beam_expert_gemm_direct(GemmParams p) {
     gemm_item_direct<KIND, G1>(p, it.x, it.y, it.z, tile);
 }
 
+// bf16: two waves per SIMD, so the 4-wave workgroups of two items overlap
+// one another's load latency (fits in 256 registers without spills); the
+// fp8 variant needs more registers and keeps one.
 template <int KIND, bool G1>
-__global__ __launch_bounds__(256) void beam_expert_gemm_lds(GemmParams p) {
+__global__ __launch_bounds__(256, KIND == W_BF16 ? 2 : 1) void beam_expert_gemm_lds(GemmParams p) {
     __shared__ uint4 bs[2][kLdsRows * 16];
     const int item = blockIdx.x / p.n_tiles;
     const int tile = blockIdx.x - item * p.n_tiles;
