@@ -15,6 +15,7 @@
 namespace beam {
 
 constexpr int kMaxIt = 8;    // chunks of 4 per thread: H <= 8 * 1024
+constexpr int kRowGroup = 4; // expert rows whose loads are issued together
 
 // 4 consecutive elements as fp32
 template <bool BF> BEAM_DEV float4 ld4(const void* p, size_t i) {
@@ -45,7 +46,7 @@ BEAM_DEV float4 fma4(float w, float4 y, float4 m) {
 }
 
 // One workgroup per token; thread i owns the 4-element chunks i, i+256, ...
-template <bool YBF, bool ABF>
+template <bool YBF, bool ABF, int NIT>
 __global__ __launch_bounds__(256) void beam_combine_norm(CombineArgs a) {
     __shared__ float red[4];
     const int t = blockIdx.x, tid = threadIdx.x;
@@ -54,26 +55,40 @@ __global__ __launch_bounds__(256) void beam_combine_norm(CombineArgs a) {
     const int32_t* prow = a.pair_row + (size_t)t * K;
     const float* wrow = a.w + (size_t)t * K;
 
-    float4 m[kMaxIt];
+    float4 m[NIT];
 #pragma unroll
-    for (int it = 0; it < kMaxIt; ++it) m[it] = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-    for (int k = 0; k < K; ++k) {
-        const int r = prow[k];
-        if ((unsigned)r >= (unsigned)TK) continue;   // never read outside y
-        const float wk = wrow[k];
-        const size_t base = (size_t)r * H;
+    for (int it = 0; it < NIT; ++it) m[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+    // K expert rows, 8 at a time: indices and weights first, then every
+    // row load of the group in flight together
+    for (int k0 = 0; k0 < K; k0 += kRowGroup) {
+        int rr[kRowGroup];
+        float wk[kRowGroup];
 #pragma unroll
-        for (int it = 0; it < kMaxIt; ++it) {
-            const int i = (it * 256 + tid) * 4;
-            if (i < H) m[it] = fma4(wk, ld4<YBF>(a.y, base + i), m[it]);
+        for (int j = 0; j < kRowGroup; ++j) {
+            const int k = k0 + j;
+            const int r = k < K ? prow[k] : -1;
+            rr[j] = ((unsigned)r < (unsigned)TK) ? r : -1;   // never read outside y
+            wk[j] = k < K ? wrow[k] : 0.f;
         }
+        float4 yv[kRowGroup][NIT];
+#pragma unroll
+        for (int j = 0; j < kRowGroup; ++j)
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) {
+                const int i = (it * 256 + tid) * 4;
+                yv[j][it] = (rr[j] >= 0 && i < H) ? ld4<YBF>(a.y, (size_t)rr[j] * H + i)
+                                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+        for (int j = 0; j < kRowGroup; ++j)
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) m[it] = fma4(wk[j], yv[j][it], m[it]);
     }
 
     // post-norm
     float ss = 0.f;
 #pragma unroll
-    for (int it = 0; it < kMaxIt; ++it)
+    for (int it = 0; it < NIT; ++it)
         if ((it * 256 + tid) * 4 < H)
             ss += (m[it].x * m[it].x + m[it].y * m[it].y) + (m[it].z * m[it].z + m[it].w * m[it].w);
     ss = block_sum<4>(ss, red);
@@ -83,7 +98,7 @@ __global__ __launch_bounds__(256) void beam_combine_norm(CombineArgs a) {
     const size_t rowo = (size_t)t * H;
     float ss2 = 0.f;
 #pragma unroll
-    for (int it = 0; it < kMaxIt; ++it) {
+    for (int it = 0; it < NIT; ++it) {
         const int i = (it * 256 + tid) * 4;
         if (i < H) {
             if (a.moe_out) *reinterpret_cast<float4*>(a.moe_out + rowo + i) = m[it];
@@ -101,7 +116,7 @@ __global__ __launch_bounds__(256) void beam_combine_norm(CombineArgs a) {
     ss2 = block_sum<4>(ss2, red);
     const float rinv2 = 1.0f / sqrtf(ss2 / (float)H + a.eps);
 #pragma unroll
-    for (int it = 0; it < kMaxIt; ++it) {
+    for (int it = 0; it < NIT; ++it) {
         const int i = (it * 256 + tid) * 4;
         if (i < H) {
             st4<ABF>(a.h, rowo + i, m[it]);
@@ -113,14 +128,28 @@ __global__ __launch_bounds__(256) void beam_combine_norm(CombineArgs a) {
     }
 }
 
-hipError_t launch_combine_norm(const CombineArgs& a, hipStream_t st) {
+template <int NIT>
+static void launch_nit(const CombineArgs& a, hipStream_t st) {
     dim3 grid(a.T), block(256);
     if (a.y_bf16) {
-        if (a.act_bf16) hipLaunchKernelGGL((beam_combine_norm<true, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((beam_combine_norm<true, false>), grid, block, 0, st, a);
+        if (a.act_bf16) hipLaunchKernelGGL((beam_combine_norm<true, true, NIT>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((beam_combine_norm<true, false, NIT>), grid, block, 0, st, a);
     } else {
-        if (a.act_bf16) hipLaunchKernelGGL((beam_combine_norm<false, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((beam_combine_norm<false, false>), grid, block, 0, st, a);
+        if (a.act_bf16) hipLaunchKernelGGL((beam_combine_norm<false, true, NIT>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((beam_combine_norm<false, false, NIT>), grid, block, 0, st, a);
+    }
+}
+
+hipError_t launch_combine_norm(const CombineArgs& a, hipStream_t st) {
+    switch ((a.H + 1023) / 1024) {   // 4-element chunks per thread
+        case 1: launch_nit<1>(a, st); break;
+        case 2: launch_nit<2>(a, st); break;
+        case 3: launch_nit<3>(a, st); break;
+        case 4: launch_nit<4>(a, st); break;
+        case 5: launch_nit<5>(a, st); break;
+        case 6: launch_nit<6>(a, st); break;
+        case 7: launch_nit<7>(a, st); break;
+        default: launch_nit<kMaxIt>(a, st); break;
     }
     return hipGetLastError();
 }
