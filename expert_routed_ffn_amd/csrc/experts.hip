@@ -48,8 +48,10 @@ __global__ __launch_bounds__(256) void beam_build_items(const int32_t* __restric
     const int nch = (cnt + MC - 1) / MC;
     int total;
     const int first = block_exclusive_scan(nch, tmp, &total);
+    // .w = 1 when the expert has more than one item: its weights are then
+    // read by several workgroups and should stay cacheable
     for (int c = 0; c < nch; ++c)
-        items[first + c] = make_int4(e, offsets[e] + c * MC, min(MC, cnt - c * MC), 0);
+        items[first + c] = make_int4(e, offsets[e] + c * MC, min(MC, cnt - c * MC), nch > 1 ? 1 : 0);
     if (e == 0) *n_items = total;
 }
 
@@ -231,7 +233,7 @@ constexpr int kLdsRows = 128;
 // hit 16 different bank groups.
 BEAM_DEV int lds_pos(int rr, int c) { return rr * 16 + (c ^ (rr & 15)); }
 
-template <int KIND, bool G1, int NB>
+template <int KIND, bool G1, int NB, bool NT>
 BEAM_DEV void gemm_item_lds(const GemmParams& p, int e, int row0, int rows, int tile,
                             uint4 (*bs)[kLdsRows * 16]) {
     constexpr int ES = (KIND == W_BF16) ? 2 : 1;
@@ -276,8 +278,13 @@ BEAM_DEV void gemm_item_lds(const GemmParams& p, int e, int row0, int rows, int 
     auto aload = [&](int buf, int k) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            wa0[buf][s] = ld16_nt(pa0 + (size_t)k * 16 + 1024 * s);
-            wa1[buf][s] = ld16_nt(pa1 + (size_t)k * 16 + 1024 * s);
+            if constexpr (NT) {
+                wa0[buf][s] = ld16_nt(pa0 + (size_t)k * 16 + 1024 * s);
+                wa1[buf][s] = ld16_nt(pa1 + (size_t)k * 16 + 1024 * s);
+            } else {
+                wa0[buf][s] = ld16(pa0 + (size_t)k * 16 + 1024 * s);
+                wa1[buf][s] = ld16(pa1 + (size_t)k * 16 + 1024 * s);
+            }
         }
     };
     // one K step on LDS buffer CUR; prefetches step kit+1 into the other buffer
@@ -328,6 +335,18 @@ __global__ __launch_bounds__(256) void beam_expert_gemm_direct(GemmParams p) {
     gemm_item_direct<KIND, G1>(p, it.x, it.y, it.z, tile);
 }
 
+template <int KIND, bool G1, bool NT>
+BEAM_DEV void dispatch_lds(const GemmParams& p, int4 it, int tile, uint4 (*bs)[kLdsRows * 16]) {
+    if (it.z <= 16)
+        gemm_item_lds<KIND, G1, 1, NT>(p, it.x, it.y, it.z, tile, bs);
+    else if (it.z <= 32)
+        gemm_item_lds<KIND, G1, 2, NT>(p, it.x, it.y, it.z, tile, bs);
+    else if (it.z <= 64)
+        gemm_item_lds<KIND, G1, 4, NT>(p, it.x, it.y, it.z, tile, bs);
+    else
+        gemm_item_lds<KIND, G1, 8, NT>(p, it.x, it.y, it.z, tile, bs);
+}
+
 // bf16: two waves per SIMD, so the 4-wave workgroups of two items overlap
 // one another's load latency (fits in 256 registers without spills); the
 // fp8 variant needs more registers and keeps one.
@@ -338,14 +357,10 @@ __global__ __launch_bounds__(256, KIND == W_BF16 ? 2 : 1) void beam_expert_gemm_
     const int tile = blockIdx.x - item * p.n_tiles;
     if (item >= *p.n_items) return;
     const int4 it = p.items[item];
-    if (it.z <= 16)
-        gemm_item_lds<KIND, G1, 1>(p, it.x, it.y, it.z, tile, bs);
-    else if (it.z <= 32)
-        gemm_item_lds<KIND, G1, 2>(p, it.x, it.y, it.z, tile, bs);
-    else if (it.z <= 64)
-        gemm_item_lds<KIND, G1, 4>(p, it.x, it.y, it.z, tile, bs);
-    else
-        gemm_item_lds<KIND, G1, 8>(p, it.x, it.y, it.z, tile, bs);
+    // weights read once (single-item expert): non-temporal; shared by the
+    // expert's other items: plain loads that stay in L2
+    if (it.w == 0) dispatch_lds<KIND, G1, true>(p, it, tile, bs);
+    else dispatch_lds<KIND, G1, false>(p, it, tile, bs);
 }
 
 // Per-row e4m3 re-quantisation of the fp32 SwiGLU output (fp8 path).
