@@ -3,15 +3,22 @@
 
 A step is one pass of the whole layer (route -> permute -> experts ->
 combine_norm) over one batch of seeded synthetic tokens, with the inputs
-and all 256 experts' weights resident in HBM.  Default workload: the Beam
-decode shape, T = 8 tokens, bf16 experts.  Prints one JSON line.
+and all 256 experts' weights resident in HBM.  The headline line is the
+Beam decode shape (T = 8 tokens, bf16 experts); the same JSON line carries
+the other shapes the metric is quoted on (T = 64 with skewed routes,
+T = 2048 prefill, T = 16384 with fp8 experts, and T = 16384 with bf16
+experts) under "configs".  Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--all]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--configs a,b|none]
 
-The roofline object describes the dominant kernel (GEMM1: gate/up
-projection + SwiGLU), timed with HIP events recorded on the stream it runs
-on, inside the timed region.  The cpu_baseline object times the CPU oracle
-on a bounded sample of the same workload.
+Timing: HIP events recorded on the launch stream around every C-ABI call
+of every timed step (route, permute, experts, combine_norm), plus one pair
+around the whole timed region; `ms_per_step` is the region over K.  The
+`roofline` object describes the dominant call, beam_moe_experts (its
+work-item, GEMM1 + SwiGLU and GEMM2 kernels), against HBM or MFMA peak
+depending on the rows per touched expert.  A hipGraph replay of the same
+step is timed as well.  `cpu_baseline` times the CPU oracle on a bounded
+sample of the same workload.
 """
 
 from __future__ import annotations
@@ -21,6 +28,7 @@ import ctypes
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -30,17 +38,22 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 BF16_MFMA_TFLOPS = 2500.0        # dense
 FP8_MFMA_TFLOPS = 5000.0
+RIDGE_ROWS = 312.5               # rows per expert where weight streaming stops bounding (bf16 and fp8)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 EXPERTS_SRC = os.path.join(ROOT, "expert_routed_ffn_amd", "csrc", "experts.hip")
+DEFAULT_CONFIGS = "skew_t64,prefill_t2048,prefill_fp8_t16384,prefill_bf16_t16384"
+METRIC = "MoE-layer tokens/s (one Beam MoE layer forward incl. routing and norm boundary)"
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_t8")
-    ap.add_argument("--all", action="store_true", help="also time the other Beam workloads")
+    ap.add_argument("--configs", default=DEFAULT_CONFIGS,
+                    help="comma-separated extra workloads timed into the same line, or 'none'")
+    ap.add_argument("--no-graph", action="store_true", help="skip the hipGraph replay timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=8)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -49,14 +62,12 @@ def parse():
 
 
 class HipEvents:
-    """Raw hipEvent_t handles (ctypes), so the library can record them on its
-    own launch stream."""
+    """Raw hipEvent_t handles (ctypes) recorded on the launch stream."""
 
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so")
         self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
-        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def create(self):
@@ -104,89 +115,155 @@ def layer_setup(wl, stacks, dev):
     import torch
     import expert_routed_ffn_amd as beam
     import synth
-    cfg = beam.LayerCfg(wl.hidden, wl.n_experts, wl.n_groups, wl.topk_groups, wl.topk,
-                        wl.group_topn, wl.d_ff, wl.routed_scale, wl.rms_eps)
     w_r, bias = synth.make_router(wl, dev)
     x, h, gp, gq = synth.make_activations(wl, dev)
     fp8 = wl.w_dtype == "fp8"
     w_dt = beam.BEAM_FP8_E4M3 if fp8 else beam.BEAM_BF16
-    bufs = beam.alloc_buffers(cfg, wl.T, x.dtype, w_dt, y_dtype=torch.bfloat16 if fp8 else torch.float32,
+    bufs = beam.alloc_buffers(lcfg(wl), wl.T, x.dtype, w_dt, y_dtype=torch.bfloat16 if fp8 else torch.float32,
                               device=dev)
     wgu, wd, sgu, sd = stacks
-    state = dict(cfg=cfg, w_r=w_r, bias=bias, x=x, h=h.clone(), h0=h, gp=gp, gq=gq, bufs=bufs,
-                 wgu=wgu, wd=wd, sgu=sgu, sd=sd)
-    return state
+    return dict(cfg=lcfg(wl), w_r=w_r, bias=bias, x=x, h=h.clone(), h0=h, gp=gp, gq=gq, bufs=bufs,
+                wgu=wgu, wd=wd, sgu=sgu, sd=sd, fp8=fp8)
 
 
-def run_step(wl, s, events=None):
+def run_step(wl, s, hipev=None, evs=None, stream=None):
+    """One layer step through the four C-ABI calls; with evs (5 events) an
+    event is recorded on the launch stream before the first call and after
+    each call."""
     import expert_routed_ffn_amd as beam
-    beam.moe_layer(s["cfg"], s["x"], s["w_r"], s["bias"], s["wgu"], s["wd"], s["h"], s["gp"], s["gq"],
-                   wl.n, s["bufs"], s_gate_up=s["sgu"], s_down=s["sd"], events=events)
+    cfg, b = s["cfg"], s["bufs"]
+    mark = (lambda i: hipev.record(evs[i], stream)) if evs is not None else (lambda i: None)
+    mark(0)
+    beam.beam_moe_route(cfg, s["x"], s["w_r"], s["bias"], b.topk_ids, b.topk_w, b.logits, b.ws)
+    mark(1)
+    beam.beam_moe_permute(cfg, b.topk_ids, b.expert_offsets, b.row_token, b.pair_row,
+                          x=s["x"] if s["fp8"] else None, x_q=b.x_q, x_scale=b.x_scale, ws=b.ws)
+    mark(2)
+    beam.beam_moe_experts(cfg, wl.T, b.x_q if s["fp8"] else s["x"], b.expert_offsets, b.row_token,
+                          s["wgu"], s["wd"], b.y, x_scale=b.x_scale, s_gate_up=s["sgu"], s_down=s["sd"],
+                          ws=b.ws)
+    mark(3)
+    beam.beam_moe_combine_norm(cfg, b.y, b.pair_row, b.topk_w, s["h"], b.x_next, s["gp"], s["gq"], wl.n,
+                               b.moe_out)
+    mark(4)
 
 
-def time_workload(wl, stacks, steps, warmup, hipev, dev):
-    """Returns dict with ms/step, GEMM1/GEMM2 average ms, touched experts."""
+def stats(v):
+    return {"median": round(statistics.median(v), 2), "min": round(min(v), 2),
+            "mean": round(sum(v) / len(v), 2)}
+
+
+def time_workload(wl, stacks, steps, warmup, hipev, dev, graph=True):
+    """Per-step stage times (µs), the timed region per step, touched experts
+    and (optionally) the hipGraph replay time per step."""
     import torch
     s = layer_setup(wl, stacks, dev)
     stream = torch.cuda.current_stream().cuda_stream
-    evs = [[hipev.create() for _ in range(4)] for _ in range(steps)]
+    evs = [[hipev.create() for _ in range(5)] for _ in range(steps)]
     t0, t1 = hipev.create(), hipev.create()
     for _ in range(warmup):
         run_step(wl, s)
     torch.cuda.synchronize()
     hipev.record(t0, stream)
     for i in range(steps):
-        run_step(wl, s, events=evs[i])
+        run_step(wl, s, hipev, evs[i], stream)
     hipev.record(t1, stream)
     torch.cuda.synchronize()
-    total_ms = hipev.elapsed_ms(t0, t1)
-    g1 = sum(hipev.elapsed_ms(e[0], e[1]) for e in evs) / steps
-    g2 = sum(hipev.elapsed_ms(e[2], e[3]) for e in evs) / steps
+    region_ms = hipev.elapsed_ms(t0, t1)
+    per = {k: [] for k in ("layer", "route", "permute", "experts", "combine_norm")}
+    for e in evs:
+        per["layer"].append(hipev.elapsed_ms(e[0], e[4]) * 1e3)
+        per["route"].append(hipev.elapsed_ms(e[0], e[1]) * 1e3)
+        per["permute"].append(hipev.elapsed_ms(e[1], e[2]) * 1e3)
+        per["experts"].append(hipev.elapsed_ms(e[2], e[3]) * 1e3)
+        per["combine_norm"].append(hipev.elapsed_ms(e[3], e[4]) * 1e3)
     offs = s["bufs"].expert_offsets.cpu()
     D = int(((offs[1:] - offs[:-1]) > 0).sum())
-    return dict(ms_per_step=total_ms / steps, gemm1_ms=g1, gemm2_ms=g2, touched=D, state=s)
+    out = dict(ms_per_step=region_ms / steps, per=per, touched=D, state=s)
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run_step(wl, s)
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        cs = torch.cuda.current_stream().cuda_stream
+        hipev.record(t0, cs)
+        for _ in range(steps):
+            g.replay()
+        hipev.record(t1, cs)
+        torch.cuda.synchronize()
+        out["graph_us_per_layer"] = hipev.elapsed_ms(t0, t1) * 1e3 / steps
+        del g
+    return out
 
 
 def algorithmic(wl, D):
-    """Algorithmic bytes and flops of GEMM1, GEMM2 and the whole layer.
-
-    Per touched expert: gate/up 2*F*H weights, down H*F weights (2 bytes bf16,
-    1 byte fp8 plus per-row fp32 scales).  Flops per (token, expert) pair:
-    2*H*2F (GEMM1) + 2*F*H (GEMM2)."""
+    """Algorithmic bytes and flops (what the method itself must move and
+    compute): the touched experts' weights (+ fp8 per-row scales), W_r,
+    and x, h in, h' and x_next out.  Permuted copies, the SwiGLU
+    intermediate and the expert outputs y are not credited.
+    Flops per (token, expert) pair: 2*H*2F (GEMM1) + 2*F*H (GEMM2)."""
     H, F, T, K, E = wl.hidden, wl.d_ff, wl.T, wl.topk, wl.n_experts
-    es = 1 if wl.w_dtype == "fp8" else 2
-    TK = T * K
-    g1_w = D * (2 * F * H * es + (2 * F * 4 if es == 1 else 0))
-    g1_bytes = g1_w + T * H * es + TK * F * (4 if es == 1 else 2)
-    g2_w = D * (H * F * es + (H * 4 if es == 1 else 0))
-    g2_bytes = g2_w + TK * F * (1 if es == 1 else 2) + TK * H * (2 if es == 1 else 4)
-    layer_bytes = g1_w + g2_w + E * H * 4 + 4 * T * H * 2   # weights + W_r + x, h, h', x_next
-    g1_flops = 2 * TK * H * 2 * F
-    g2_flops = 2 * TK * F * H
-    return dict(g1_bytes=g1_bytes, g2_bytes=g2_bytes, layer_bytes=layer_bytes, g1_flops=g1_flops,
-                g2_flops=g2_flops, router_flops=2 * T * H * E)
+    fp8 = wl.w_dtype == "fp8"
+    es = 1 if fp8 else 2
+    w_expert = 3 * H * F * es + ((2 * F + H) * 4 if fp8 else 0)
+    x_read = T * H * (1 if fp8 else 2) + (T * 4 if fp8 else 0)     # the GEMM input: e4m3 codes + scales, or bf16
+    experts_bytes = D * w_expert + x_read
+    layer_bytes = D * w_expert + E * H * 4 + 4 * T * H * 2
+    experts_flops = 6 * H * F * T * K
+    return dict(w_expert=w_expert, experts_bytes=experts_bytes, layer_bytes=layer_bytes,
+                experts_flops=experts_flops, layer_flops=experts_flops + 2 * T * H * E)
 
 
-def traffic_for(workload, kernel):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None if it is missing or was taken on a different kernel source."""
+def traffic_for(workload):
+    """Measured HBM bytes per beam_moe_experts call from the committed
+    rocprofv3 counter summary, or None if it is missing or was taken on a
+    different expert-kernel source."""
     try:
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    rec = t.get(workload, {}).get(kernel)
+    rec = t.get(workload, {}).get("experts")
     if not rec or rec.get("kernel_src_hash") != kernel_hash():
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get("bytes_per_call")
+
+
+def roofline_entry(wl, r):
+    """Roofline of the dominant call (beam_moe_experts) and of the layer."""
+    D = r["touched"]
+    alg = algorithmic(wl, D)
+    fp8 = wl.w_dtype == "fp8"
+    ex_us = sum(r["per"]["experts"]) / len(r["per"]["experts"])
+    ex_s = ex_us / 1e6
+    rows_per_expert = wl.T * wl.topk / max(D, 1)
+    if rows_per_expert >= RIDGE_ROWS:
+        peak = FP8_MFMA_TFLOPS if fp8 else BF16_MFMA_TFLOPS
+        ach = alg["experts_flops"] / ex_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4), "algorithmic_flops": alg["experts_flops"]}
+    else:
+        ach = alg["experts_bytes"] / ex_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "algorithmic_bytes": alg["experts_bytes"]}
+    roof.update({"traffic": traffic_for(wl.name),
+                 "kernel": "beam_moe_experts call (work items, GEMM1 + SwiGLU, GEMM2"
+                           + (", e4m3 re-quantisation of a" if fp8 else "") + ")",
+                 "kernel_avg_us": round(ex_us, 2)})
+    step_s = r["ms_per_step"] / 1e3
+    peak_f = FP8_MFMA_TFLOPS if fp8 else BF16_MFMA_TFLOPS
+    layer = {"hbm_frac": round(alg["layer_bytes"] / step_s / 1e9 / HBM_PEAK_GBS, 4),
+             "mfma_frac": round(alg["layer_flops"] / step_s / 1e12 / peak_f, 4),
+             "algorithmic_bytes": alg["layer_bytes"], "algorithmic_flops": alg["layer_flops"]}
+    return roof, layer
 
 
 def cpu_baseline(wl, state, n_tokens, min_seconds=10.0, max_reps=8):
-    """Times the CPU oracle on the first n_tokens tokens of the workload (all
-    of them for the decode shape), repeating the pass until at least
-    min_seconds of CPU work have been timed.  The experts' plain bf16 weights
-    are staged on the host before the clock starts; the oracle widens them
-    to fp64 itself as part of its work."""
-    import numpy as np
+    """Times the CPU oracle on the first n_tokens tokens of the workload,
+    repeating the pass until at least min_seconds of CPU work have been
+    timed.  The experts' plain weights are staged on the host before the
+    clock starts; the oracle widens them to fp64 itself as part of its work."""
     import torch
     import oracle
     import synth
@@ -200,7 +277,6 @@ def cpu_baseline(wl, state, n_tokens, min_seconds=10.0, max_reps=8):
                 hidden=wl.hidden, d_ff=wl.d_ff, rms_eps=wl.rms_eps)
     routes = oracle.route(oracle.router_logits(xn, w_r), bias, ocfg)
     need = sorted({int(e) for r in routes for e in r.ids})
-    # plain row-major weights of the needed experts, staged on the host before the clock
     host = {}
     for e in need:
         a, b, c, d = synth.make_expert(wl, e, s["x"].device)
@@ -220,10 +296,25 @@ def cpu_baseline(wl, state, n_tokens, min_seconds=10.0, max_reps=8):
         dt += time.perf_counter() - t0
         reps += 1
     cores = len(os.sched_getaffinity(0))
-    return {"value": len(tokens) * reps / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": round(len(tokens) * reps / dt, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{len(tokens)} of the {wl.T} tokens of {wl.name} through the whole layer (router, "
-                      f"selection, the {len(need)} experts they use as fp64 SwiGLU MLPs, combine, norm "
-                      f"boundary), {reps} passes, {dt:.1f} s on {cores} host threads"}
+                      f"selection, the {len(need)} experts they use as fp64 SwiGLU MLPs"
+                      f"{' with e4m3 activations' if fp8 else ''}, combine, norm boundary), "
+                      f"{reps} passes, {dt:.1f} s on {cores} host threads"}
+
+
+def entry(wl, r):
+    roof, layer = roofline_entry(wl, r)
+    sec = r["ms_per_step"] / 1e3
+    e = {"us_per_layer": round(r["ms_per_step"] * 1e3, 1),
+         "tokens_per_s": round(wl.T / sec, 1),
+         "T": wl.T, "expert_weights": wl.w_dtype, "experts_touched": r["touched"],
+         "layer_us": stats(r["per"]["layer"]),
+         "stages_us_median": {k: round(statistics.median(v), 2) for k, v in r["per"].items() if k != "layer"},
+         "roofline": roof, "layer_roofline": layer}
+    if "graph_us_per_layer" in r:
+        e["graph_us_per_layer"] = round(r["graph_us_per_layer"], 1)
+    return e
 
 
 def main():
@@ -257,36 +348,20 @@ def main():
     hipev = HipEvents()
 
     wl = synth.WORKLOADS[args.workload]
-    stacks = packed_stacks(wl, dev)
-    torch.cuda.synchronize()
-    r = time_workload(wl, stacks, args.steps, args.warmup, hipev, dev)
-    D = r["touched"]
-    alg = algorithmic(wl, D)
+    by_dtype = {wl.w_dtype: packed_stacks(wl, dev)}
+    r = time_workload(wl, by_dtype[wl.w_dtype], args.steps, args.warmup, hipev, dev, graph=not args.no_graph)
+    main_entry = entry(wl, r)
+    print(f"# {wl.name}: {main_entry['us_per_layer']} us/layer", file=sys.stderr, flush=True)
     fp8 = wl.w_dtype == "fp8"
-    g1_s = r["gemm1_ms"] / 1e3
-    achieved = alg["g1_bytes"] / g1_s / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic_for(wl.name, "gemm1"),
-                "kernel": "beam_expert_gemm (GEMM1 gate/up + SwiGLU)",
-                "kernel_avg_us": round(r["gemm1_ms"] * 1e3, 2),
-                "algorithmic_bytes": alg["g1_bytes"]}
-    if wl.T * wl.topk / max(D, 1) >= 315 * (2 if fp8 else 1):
-        peak = FP8_MFMA_TFLOPS if fp8 else BF16_MFMA_TFLOPS
-        ach = alg["g1_flops"] / g1_s / 1e12
-        roofline.update({"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
-                         "frac": round(ach / peak, 4)})
-    step_s = r["ms_per_step"] / 1e3
-    layer_hbm = alg["layer_bytes"] / step_s / 1e9
     out = {
-        "metric": "MoE-layer tokens/s (one Beam MoE layer forward incl. routing and norm boundary)",
-        "value": round(wl.T / step_s, 1),
+        "metric": METRIC,
+        "value": main_entry["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(r["ms_per_step"], 4),
-        "us_per_layer": round(r["ms_per_step"] * 1e3, 1),
+        "us_per_layer": main_entry["us_per_layer"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -294,36 +369,32 @@ def main():
         "data": "synthetic (seeded; all 256 experts resident in HBM)",
         "config": {"workload": wl.name, "T": wl.T, "hidden": wl.hidden, "n_experts": wl.n_experts,
                    "groups": f"{wl.topk_groups}/{wl.n_groups}", "topk": wl.topk, "d_ff": wl.d_ff,
-                   "expert_weights": wl.w_dtype, "router": "fp32", "experts_touched": D,
+                   "expert_weights": wl.w_dtype, "router": "fp32", "experts_touched": r["touched"],
                    "parallelism": "single GPU"},
-        "roofline": roofline,
-        "layer_hbm": {"achieved": round(layer_hbm, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                      "frac": round(layer_hbm / HBM_PEAK_GBS, 4), "algorithmic_bytes": alg["layer_bytes"]},
-        "kernels_us": {"gemm1": round(r["gemm1_ms"] * 1e3, 2), "gemm2": round(r["gemm2_ms"] * 1e3, 2)},
+        "roofline": main_entry["roofline"],
+        "layer_roofline": main_entry["layer_roofline"],
+        "layer_us": main_entry["layer_us"],
+        "stages_us_median": main_entry["stages_us_median"],
     }
-    if args.all:
-        extra = {}
-        names = [n for n in synth.WORKLOAD_ORDER if n not in ("tiny_fp32", wl.name)]
-        by_dtype = {wl.w_dtype: stacks}
-        for name in names:
-            w2 = synth.WORKLOADS[name]
-            if w2.w_dtype not in by_dtype:
-                by_dtype[w2.w_dtype] = packed_stacks(w2, dev)
-            r2 = time_workload(w2, by_dtype[w2.w_dtype], max(3, args.steps // 5), 2, hipev, dev)
-            a2 = algorithmic(w2, r2["touched"])
-            fl = a2["g1_flops"] + a2["g2_flops"]
-            peak = FP8_MFMA_TFLOPS if w2.w_dtype == "fp8" else BF16_MFMA_TFLOPS
-            sec = r2["ms_per_step"] / 1e3
-            extra[name] = {"us_per_layer": round(r2["ms_per_step"] * 1e3, 1),
-                           "tokens_per_s": round(w2.T / sec, 1),
-                           "experts_touched": r2["touched"],
-                           "hbm_frac": round(a2["layer_bytes"] / sec / 1e9 / HBM_PEAK_GBS, 4),
-                           "mfma_frac": round(fl / sec / 1e12 / peak, 4),
-                           "gemm1_us": round(r2["gemm1_ms"] * 1e3, 1), "gemm2_us": round(r2["gemm2_ms"] * 1e3, 1)}
-            del r2
-        out["other_workloads"] = extra
+    if "graph_us_per_layer" in main_entry:
+        out["graph_us_per_layer"] = main_entry["graph_us_per_layer"]
+    state_main = r["state"]
+    names = [] if args.configs == "none" else [n for n in args.configs.split(",") if n and n != wl.name]
+    cfgs = {}
+    for name in names:
+        w2 = synth.WORKLOADS[name]
+        if w2.w_dtype not in by_dtype:
+            by_dtype[w2.w_dtype] = packed_stacks(w2, dev)
+        r2 = time_workload(w2, by_dtype[w2.w_dtype], args.steps, min(args.warmup, 3), hipev, dev,
+                           graph=not args.no_graph)
+        cfgs[name] = entry(w2, r2)
+        print(f"# {name}: {cfgs[name]['us_per_layer']} us/layer", file=sys.stderr, flush=True)
+        del r2
+        torch.cuda.empty_cache()
+    if cfgs:
+        out["configs"] = cfgs
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, r["state"], args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(wl, state_main, args.cpu_tokens)
     print(json.dumps(out), flush=True)
 
 

@@ -81,7 +81,7 @@ def lib() -> ctypes.CDLL:
     L.beam_moe_route.argtypes = [cfgp, i32, vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.beam_moe_permute.argtypes = [cfgp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
     L.beam_moe_experts.argtypes = [cfgp, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32,
-                                   vp, sz, vp, vp]
+                                   vp, sz, vp]
     L.beam_moe_combine_norm.argtypes = [cfgp, i32, vp, i32, vp, vp, vp, vp, i32, vp, vp, i32, vp, vp]
     L.beam_moe_pack_weights.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp]
     L.beam_moe_workspace_bytes.argtypes = [cfgp, i32, i32]
@@ -185,7 +185,7 @@ def beam_moe_permute(cfg: LayerCfg, topk_ids, expert_offsets, row_token, pair_ro
 
 
 def beam_moe_experts(cfg: LayerCfg, T, x, expert_offsets, row_token, w_gate_up, w_down, y,
-                     x_scale=None, s_gate_up=None, s_down=None, ws=None, stream=None, events=None):
+                     x_scale=None, s_gate_up=None, s_down=None, ws=None, stream=None):
     """x: [T,H] f32/bf16 activations, or e4m3 codes (uint8) for fp8 weights."""
     E, H, F, TK = cfg.n_experts, cfg.hidden, cfg.d_ff, T * cfg.topk
     w_dt = _dt(w_gate_up)
@@ -199,14 +199,10 @@ def beam_moe_experts(cfg: LayerCfg, T, x, expert_offsets, row_token, w_gate_up, 
         _check(x_scale, (T,), (torch.float32,), "x_scale")
         _check(s_gate_up, (E, 2 * F), (torch.float32,), "s_gate_up")
         _check(s_down, (E, H), (torch.float32,), "s_down")
-    ev = None
-    if events is not None:
-        ev = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e) for e in events])
     st = lib().beam_moe_experts(ctypes.byref(cfg.c()), T, w_dt, _p(x), w_dt, _p(x_scale),
                                 _p(expert_offsets), _p(row_token), _p(w_gate_up), _p(s_gate_up),
                                 _p(w_down), _p(s_down), _p(y), _dt(y), _p(ws),
-                                0 if ws is None else ws.numel(), _stream(stream),
-                                ctypes.cast(ev, ctypes.c_void_p) if ev is not None else None)
+                                0 if ws is None else ws.numel(), _stream(stream))
     _ok("beam_moe_experts", st)
 
 
@@ -307,7 +303,7 @@ def alloc_buffers(cfg: LayerCfg, T: int, act_dtype, w_dtype: int, y_dtype=torch.
 
 
 def moe_layer(cfg: LayerCfg, x, w_router, bias, w_gate_up, w_down, h, gamma_post, gamma_pre, n,
-              bufs: LayerBuffers, s_gate_up=None, s_down=None, stream=None, events=None):
+              bufs: LayerBuffers, s_gate_up=None, s_down=None, stream=None):
     """Runs the four entry points in order on one stream.  w_gate_up/w_down
     are packed stacks (beam_moe_pack_weights).  h is updated in place; the
     other results land in `bufs`."""
@@ -319,6 +315,6 @@ def moe_layer(cfg: LayerCfg, x, w_router, bias, w_gate_up, w_down, h, gamma_post
                      stream=stream)
     beam_moe_experts(cfg, T, bufs.x_q if fp8 else x, bufs.expert_offsets, bufs.row_token,
                      w_gate_up, w_down, bufs.y, x_scale=bufs.x_scale, s_gate_up=s_gate_up,
-                     s_down=s_down, ws=bufs.ws, stream=stream, events=events)
+                     s_down=s_down, ws=bufs.ws, stream=stream)
     beam_moe_combine_norm(cfg, bufs.y, bufs.pair_row, bufs.topk_w, h, bufs.x_next, gamma_post,
                           gamma_pre, n, bufs.moe_out, stream)

@@ -124,7 +124,7 @@ beam_status beam_moe_permute(const beam_moe_cfg* cfg, int32_t T, const int32_t* 
         if (!aligned16(x) || !aligned16(x_q)) return BEAM_ERR_INVALID_ARG;
     }
     const size_t need = beam::permute_ws_bytes(T, cfg->topk, cfg->n_experts);
-    if (need > 0 && (!ws || ws_bytes < need)) return BEAM_ERR_WORKSPACE;
+    if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return BEAM_ERR_WORKSPACE;
     beam::PermuteArgs a{};
     a.T = T;
     a.K = cfg->topk;
@@ -146,7 +146,7 @@ beam_status beam_moe_experts(const beam_moe_cfg* cfg, int32_t T, beam_dtype w_dt
                              beam_dtype x_dtype, const float* x_scale, const int32_t* expert_offsets,
                              const int32_t* row_token, const void* w_gate_up, const float* s_gate_up,
                              const void* w_down, const float* s_down, void* y, beam_dtype y_dtype,
-                             void* ws, size_t ws_bytes, void* stream, void* const* events) {
+                             void* ws, size_t ws_bytes, void* stream) {
     beam_status st = check_cfg(cfg);
     if (st != BEAM_OK) return st;
     if (T < 0 || T > kMaxT) return BEAM_ERR_INVALID_ARG;
@@ -184,7 +184,6 @@ beam_status beam_moe_experts(const beam_moe_cfg* cfg, int32_t T, beam_dtype w_dt
     a.y = y;
     a.y_bf16 = y_dtype == BEAM_BF16;
     a.ws = ws;
-    for (int i = 0; i < 4; ++i) a.ev[i] = events ? static_cast<hipEvent_t>(events[i]) : nullptr;
     return beam::launch_experts(a, static_cast<hipStream_t>(stream)) == hipSuccess ? BEAM_OK
                                                                                     : BEAM_ERR_HIP;
 }

@@ -482,22 +482,14 @@ static void launch_gemm(const GemmParams& p, int n_blocks, int mc, hipStream_t s
         hipLaunchKernelGGL((beam_expert_gemm_lds<KIND, G1>), dim3(n_blocks), dim3(256), 0, st, p);
 }
 
-static void record(hipEvent_t ev, hipStream_t st) {
-    if (ev) (void)hipEventRecord(ev, st);
-}
-
 hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st) {
     const int TK = a.T * a.K;
     ExpertsWs ws = carve(a.ws, a.T, a.K, a.E, a.F, a.w);
     if (a.w == W_F32) {
-        record(a.ev[0], st);
         hipLaunchKernelGGL(beam_expert_f32_gemm1, dim3(TK), dim3(256), 0, st, (const float*)a.x,
                            a.offsets, a.row_token, (const float*)a.wgu, a.E, a.H, a.F, (float*)ws.a);
-        record(a.ev[1], st);
-        record(a.ev[2], st);
         hipLaunchKernelGGL(beam_expert_f32_gemm2, dim3(TK), dim3(256), 0, st, (const float*)ws.a,
                            a.offsets, (const float*)a.wd, a.E, a.H, a.F, a.y, a.y_bf16);
-        record(a.ev[3], st);
         return hipGetLastError();
     }
     const int mc = rows_per_item(a.T);
@@ -520,12 +512,10 @@ hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st) {
     p.wscale = a.sgu;
     p.out = ws.a;
     p.out_bf16 = false;
-    record(a.ev[0], st);
     if (a.w == W_BF16)
         launch_gemm<W_BF16, true>(p, n_items_max * p.n_tiles, mc, st);
     else
         launch_gemm<W_FP8, true>(p, n_items_max * p.n_tiles, mc, st);
-    record(a.ev[1], st);
 
     // GEMM2
     p.n_tiles = a.H / 128;
@@ -539,15 +529,12 @@ hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st) {
                            a.offsets, a.E, a.F, ws.aq, ws.ascale);
         p.act = ws.aq;
         p.act_scale = ws.ascale;
-        record(a.ev[2], st);
         launch_gemm<W_FP8, false>(p, n_items_max * p.n_tiles, mc, st);
     } else {
         p.act = static_cast<const uint8_t*>(ws.a);
         p.act_scale = nullptr;
-        record(a.ev[2], st);
         launch_gemm<W_BF16, false>(p, n_items_max * p.n_tiles, mc, st);
     }
-    record(a.ev[3], st);
     return hipGetLastError();
 }
 

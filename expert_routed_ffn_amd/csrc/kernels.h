@@ -54,7 +54,6 @@ struct ExpertsArgs {
     void* y;
     bool y_bf16;
     void* ws;
-    hipEvent_t ev[4];       // optional timing events (null entries skipped)
 };
 size_t experts_ws_bytes(int T, int K, int E, int H, int F, WKind w);
 hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st);

@@ -28,7 +28,11 @@ BEAM_DEV void stable_scatter(const int32_t* __restrict__ ids, int begin, int end
         const int p = base + threadIdx.x;
         bool valid = p < end;
         int e = valid ? ids[p] : 0;
-        if ((unsigned)e >= (unsigned)E) { valid = false; e = 0; }   // out-of-range ids are dropped
+        if (valid && (unsigned)e >= (unsigned)E) {   // out-of-range ids are dropped
+            pair_row[p] = -1;
+            valid = false;
+            e = 0;
+        }
         uint64_t peers = __ballot(valid);
         for (int bit = 0; bit < ebits; ++bit) {
             const bool b = (e >> bit) & 1;

@@ -114,9 +114,12 @@ beam_status beam_moe_route(const beam_moe_cfg* cfg, int32_t T,
  *                   (round to nearest even, saturating at 448)
  *   x_scale         [T] fp32 out (required with x_q): amax(|x[t]|) / 448,
  *                   1 for an all-zero row
- * Ids outside [0,E) are a caller error; such pairs are dropped (they get no
- * row, pair_row is left unwritten for them and expert_offsets[E] counts only
- * the valid pairs), so no access ever leaves the buffers.
+ * Ids outside [0,E) are a caller error; such pairs are dropped: they get no
+ * row, pair_row[p] = -1 for them (beam_moe_combine_norm skips such entries)
+ * and expert_offsets[E] counts only the valid pairs, so no access ever
+ * leaves the buffers.
+ *   ws              required when T*K > 4096 (per-chunk histograms), 16-byte
+ *                   aligned; see beam_moe_workspace_bytes
  */
 beam_status beam_moe_permute(const beam_moe_cfg* cfg, int32_t T,
                              const int32_t* topk_ids,
@@ -149,8 +152,6 @@ beam_status beam_moe_permute(const beam_moe_cfg* cfg, int32_t T,
  *             (same size, tiled layout); the scales stay row-major.
  *   y         [T*K,H] out, dtype y_dtype (F32 or BF16): unweighted expert
  *             outputs in permuted row order
- *   events    nullable array of 4 hipEvent_t recorded on `stream` before
- *             GEMM1, after GEMM1, before GEMM2 and after GEMM2 (timing hook)
  */
 beam_status beam_moe_experts(const beam_moe_cfg* cfg, int32_t T, beam_dtype w_dtype,
                              const void* x, beam_dtype x_dtype, const float* x_scale,
@@ -158,8 +159,7 @@ beam_status beam_moe_experts(const beam_moe_cfg* cfg, int32_t T, beam_dtype w_dt
                              const void* w_gate_up, const float* s_gate_up,
                              const void* w_down, const float* s_down,
                              void* y, beam_dtype y_dtype,
-                             void* ws, size_t ws_bytes, void* stream,
-                             void* const* events);
+                             void* ws, size_t ws_bytes, void* stream);
 
 /*
  * beam_moe_combine_norm -- weighted combine + sandwich-norm boundary.

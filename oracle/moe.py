@@ -21,8 +21,10 @@ reason in the design notes of the repository):
   * each RMSNorm is v / sqrt(mean(v^2) + eps) * gamma with learned gamma;
   * fp8 path: dynamic per-row scale amax/448 for the token activations and
     for each (token, expert) SwiGLU output over all F columns, e4m3 codes by
-    round-to-nearest-even with saturation at +-448; that quantisation
-    decision is taken in fp32, the precision the kernel takes it in.
+    round-to-nearest-even with saturation at +-448.  The scale and the
+    division that picks each code are fp32 operations: the Gaudi port's
+    W8A8 reference is an fp32 CPU program that models per-token FP8
+    activations ([GD] "Correctness"), so its scales are fp32 numbers.
 """
 
 from __future__ import annotations
@@ -118,12 +120,14 @@ def quantize_row_e4m3(v):
     """Dynamic per-row e4m3 quantisation: returns (scale, quantised values).
 
     scale = amax / 448 so that the row's largest magnitude maps onto the
-    largest code; q = e4m3(v / scale).  The scale and the division are taken
-    in fp32, as the kernel takes them (the decision that picks each code is
-    made in one precision on both sides).  An all-zero row gets scale 1 and
-    codes 0.  ([GD] "What was built": per-channel FP8 weights with dynamic
-    per-token activations; "EP vs TP quality": the down-projection input is
-    quantised per token over the whole 2560-wide intermediate.)
+    largest code; q = e4m3(v / scale).  v is taken as fp32 values and the
+    scale and the division are fp32 operations (correctly rounded), the
+    precision of the W8A8 reference program ([GD] "Correctness": an fp32
+    CPU oracle with a W8A8 variant modelling per-token FP8 activations).
+    An all-zero row gets scale 1 and codes 0.  ([GD] "What was built":
+    per-channel FP8 weights with dynamic per-token activations; "EP vs TP
+    quality": the down-projection input is quantised per token over the
+    whole 2560-wide intermediate.)
     """
     v32 = np.asarray(v, dtype=np.float64).astype(np.float32)
     amax = np.float32(np.max(np.abs(v32))) if v32.size else np.float32(0)
@@ -284,22 +288,30 @@ def expert_ffn_w8a8(u, q_gu, s_gu, q_d, s_d):
       g_j = sx * s_gu[j] * sum_i qx_i * q_gu[j,i]    (v likewise)
       a = silu(g) * v;  (sa, qa) = quantize_row_e4m3(a) over all F
       y_o = sa * s_d[o] * sum_j qa_j * q_d[o,j]
-    The fp64 sums of e4m3 products are exact at these sizes.
+    The fp64 sums of e4m3 products are exact at these sizes (every product
+    is a multiple of 2^-18 below 2^18, so a sum of up to 2^17 of them needs
+    fewer than 53 bits), which makes the order of the summation irrelevant:
+    the rows go through one matrix product per projection.
     """
     u = np.atleast_2d(np.asarray(u, np.float64))
-    wgu = e4m3_decode(q_gu)
-    wd = e4m3_decode(q_d)
+    table = e4m3_decode(np.arange(256))          # value of every code
+    wgu = table[np.asarray(q_gu, np.uint8)]
+    wd = table[np.asarray(q_d, np.uint8)]
     s_gu = np.asarray(s_gu, np.float64)
     s_d = np.asarray(s_d, np.float64)
     F = wgu.shape[0] // 2
-    out = np.empty((u.shape[0], wd.shape[0]))
-    for r in range(u.shape[0]):
-        sx, qx = quantize_row_e4m3(u[r])
-        gv = sx * s_gu * (wgu @ qx)
-        a = silu(gv[:F]) * gv[F:]
-        sa, qa = quantize_row_e4m3(a)
-        out[r] = sa * s_d * (wd @ qa)
-    return out
+    m = u.shape[0]
+    sx = np.empty(m)
+    qx = np.empty_like(u)
+    for r in range(m):
+        sx[r], qx[r] = quantize_row_e4m3(u[r])
+    gv = sx[:, None] * s_gu[None, :] * (qx @ wgu.T)
+    a = silu(gv[:, :F]) * gv[:, F:]
+    sa = np.empty(m)
+    qa = np.empty_like(a)
+    for r in range(m):
+        sa[r], qa[r] = quantize_row_e4m3(a[r])
+    return sa[:, None] * s_d[None, :] * (qa @ wd.T)
 
 
 def combine(y, w):

@@ -71,9 +71,16 @@ WORKLOADS = {
                               seed=1, **_BEAM),
     "prefill_fp8_t16384": Workload("prefill_fp8_t16384", T=16384, n=20, act_dtype="bf16",
                                    w_dtype="fp8", bias_sigma=0.02, seed=1, **_BEAM),
+    # the fp8 prefill shape with the bf16 experts of the other Beam workloads:
+    # about 512 rows per expert, past the point where bf16 matrix-core
+    # throughput rather than HBM bandwidth bounds the expert GEMMs
+    "prefill_bf16_t16384": Workload("prefill_bf16_t16384", T=16384, n=20, act_dtype="bf16",
+                                    w_dtype="bf16", bias_sigma=0.02, seed=1, **_BEAM),
 }
-# the order the workloads are listed in (index = position in that list)
-WORKLOAD_ORDER = ["tiny_fp32", "decode_t8", "skew_t64", "prefill_t2048", "prefill_fp8_t16384"]
+# the order the workloads are listed in (index = position in that list; the
+# bf16 16384-token shape was added after the first five)
+WORKLOAD_ORDER = ["tiny_fp32", "decode_t8", "skew_t64", "prefill_t2048", "prefill_fp8_t16384",
+                  "prefill_bf16_t16384"]
 
 
 def _seed(*parts: int) -> int:

@@ -42,10 +42,33 @@ def max_abs(got, ref):
     return float(np.max(np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64)))) if np.size(ref) else 0.0
 
 
+def _bf16_ulp(v):
+    """Spacing of bfloat16 values at |v| (normal range)."""
+    e = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+def report_over(name, got, ref, bound):
+    """Prints every element whose error exceeds `bound`, with the error in
+    units of the bf16 spacing at the oracle's value (a one-ulp rounding
+    flip shows as 1.0)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    err = np.abs(got - ref)
+    idx = np.argwhere(err > bound)
+    for i in idx[:20]:
+        i = tuple(i)
+        say(f"    {name}{list(i)}: got {got[i]!r} oracle {ref[i]!r} err {err[i]:.3e} "
+            f"= {err[i] / _bf16_ulp(ref[i]):.2f} bf16 ulp")
+    return len(idx)
+
+
 def check_output(name, got, ref, kind):
     """kind: 'bf16', 'fp8' or 'f32'.  Returns (max_abs, rel_l2)."""
     ma, rl = max_abs(got, ref), rel_l2(got, ref)
-    say(f"  {name}: max_abs={ma:.3e} rel_l2={rl:.3e} ({kind})")
+    say(f"  {name}: max_abs={ma:.3e} rel_l2={rl:.3e} ({kind}, {np.size(ref)} elements)")
+    if kind == "bf16" and ma > BF16_MAXABS:
+        report_over(name, got, ref, BF16_MAXABS)
     if kind == "bf16":
         assert ma <= BF16_MAXABS and rl <= BF16_RELL2, (name, ma, rl)
     elif kind == "fp8":

@@ -87,7 +87,7 @@ def test_zero_tokens_is_a_no_op(L):
     assert L.beam_moe_route(ctypes.byref(c), 0, None, 1, None, None, None, None, None, None, 0, None) == 0
     assert L.beam_moe_permute(ctypes.byref(c), 0, None, None, None, None, None, 1, None, None, None, 0, None) == 0
     assert L.beam_moe_experts(ctypes.byref(c), 0, 1, None, 1, None, None, None, None, None, None, None,
-                              None, 0, None, 0, None, None) == 0
+                              None, 0, None, 0, None) == 0
     assert L.beam_moe_combine_norm(ctypes.byref(c), 0, None, 0, None, None, None, None, 1, None, None,
                                    1, None, None) == 0
 
@@ -101,6 +101,7 @@ def test_permute_argument_checks(L):
     assert f(xq=FAKE) == 1                 # x_q needs x and x_scale
     assert f(xq=FAKE, x=FAKE, xs=FAKE, xdt=0) == 1
     assert f(T=4096) == 3                  # multi-block permutation needs workspace
+    assert f(T=4096, ws=FAKE + 4, wsb=1 << 30) == 3   # ... 16-byte aligned
 
 
 def test_experts_argument_checks(L):
@@ -108,7 +109,7 @@ def test_experts_argument_checks(L):
 
     def f(T=8, w_dt=1, x_dt=1, xs=None, sgu=None, sd=None, y_dt=0, ws=FAKE, wsb=1 << 40, x=FAKE, y=FAKE):
         return L.beam_moe_experts(ctypes.byref(c), T, w_dt, x, x_dt, xs, FAKE, FAKE, FAKE, sgu, FAKE,
-                                  sd, y, y_dt, ws, wsb, None, None)
+                                  sd, y, y_dt, ws, wsb, None)
 
     assert f(x_dt=0) == 1                      # activation dtype must match the weights
     assert f(y_dt=2) == 1                      # y cannot be fp8

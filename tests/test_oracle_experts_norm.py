@@ -193,3 +193,54 @@ def test_layer_outputs_are_per_token():
     # fp64 BLAS may sum in another order for another row count: compare to 1e-12
     np.testing.assert_allclose(sub["m"][0], full["m"][2], rtol=1e-12, atol=1e-14)
     assert list(sub["routes"][0].ids) == list(full["routes"][2].ids)
+
+
+def test_ids_override_equals_bias_forced_selection():
+    # The correction bias only decides which experts are picked; the weights
+    # use the unbiased scores ([TS] "Architecture").  So overriding a token's
+    # experts with a set S must give exactly what the unmodified layer gives
+    # when S's experts get +100 bias (which forces S through both the group
+    # and the expert stage).  Sizes: tiny layer, 16 experts in 4 groups, keep
+    # 2 groups, K = 4; S spans groups 1 and 3 and is not the oracle's choice.
+    wl, cfg, w_r, bias, x, h, gp, gq = _tiny_inputs()
+    experts = {e: synth.make_expert(wl, e) for e in range(wl.n_experts)}
+    ew = lambda e: {"w_gu": synth.to_f64(experts[e][0]), "w_d": synth.to_f64(experts[e][1])}
+    xd, wr, b = synth.to_f64(x), synth.to_f64(w_r), synth.to_f64(bias)
+    args = (synth.to_f64(h), synth.to_f64(gp), synth.to_f64(gq), wl.n)
+    S = [13, 5, 4, 15]
+    plain = oracle.layer_tokens(cfg, xd, wr, b, ew, *args, rnd=ident)
+    assert set(plain["routes"][1].ids) != set(S)
+    over = oracle.layer_tokens(cfg, xd, wr, b, ew, *args, rnd=ident, ids_override={1: S})
+    b_forced = b.copy()
+    b_forced[S] += 100.0
+    forced = oracle.layer_tokens(cfg, xd, wr, b_forced, ew, *args, rnd=ident)
+    assert set(forced["routes"][1].ids) == set(S)
+    assert list(over["routes"][1].ids) == S
+    order = [list(forced["routes"][1].ids).index(e) for e in S]
+    np.testing.assert_allclose(over["routes"][1].weights, forced["routes"][1].weights[order], rtol=1e-15)
+    for k in ("m", "h_new", "x_next"):
+        np.testing.assert_allclose(over[k][1], forced[k][1], rtol=1e-13, atol=1e-13)
+    # tokens without an override are untouched
+    for t in (0, 2, 3):
+        assert list(over["routes"][t].ids) == list(plain["routes"][t].ids)
+        np.testing.assert_array_equal(over["m"][t], plain["m"][t])
+    # weights still sum to the routed scale and follow the unbiased scores
+    w = over["routes"][1].weights
+    assert abs(w.sum() - 2.5) < 1e-14
+    s = plain["routes"][1].scores[S]
+    np.testing.assert_allclose(w / w[0], s / s[0], rtol=1e-14)
+
+
+def test_w8a8_rows_are_independent():
+    # the batched W8A8 evaluation of several rows equals evaluating each row
+    # on its own (per-row activation and intermediate scales)
+    rng = np.random.default_rng(8)
+    H, F = 256, 128
+    u = rng.standard_normal((5, H)) * rng.uniform(0.1, 10, (5, 1))
+    q_gu = rng.integers(0, 0x7E, (2 * F, H)).astype(np.uint8) | (rng.integers(0, 2, (2 * F, H)) << 7).astype(np.uint8)
+    q_d = rng.integers(0, 0x7E, (H, F)).astype(np.uint8)
+    s_gu = rng.uniform(1e-4, 1e-3, 2 * F)
+    s_d = rng.uniform(1e-4, 1e-3, H)
+    full = oracle.expert_ffn_w8a8(u, q_gu, s_gu, q_d, s_d)
+    for r in range(5):
+        np.testing.assert_array_equal(full[r], oracle.expert_ffn_w8a8(u[r], q_gu, s_gu, q_d, s_d)[0])
