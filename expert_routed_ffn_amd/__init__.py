@@ -28,8 +28,10 @@ BEAM_F32, BEAM_BF16, BEAM_FP8_E4M3 = 0, 1, 2
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape or dtype",
           3: "workspace missing or too small", 4: "HIP launch failed"}
 
-SYMBOLS = ("beam_moe_route", "beam_moe_permute", "beam_moe_experts", "beam_moe_combine_norm",
-           "beam_moe_pack_weights", "beam_moe_workspace_bytes", "beam_moe_status_string")
+SYMBOLS = ("beam_moe_route", "beam_moe_permute", "beam_moe_experts", "beam_moe_experts_static",
+           "beam_moe_combine_norm", "beam_moe_pack_weights", "beam_moe_workspace_bytes",
+           "beam_moe_status_string")
+STATIC_SCRATCH_BYTES = 64 << 20   # BEAM_MOE_STATIC_SCRATCH_BYTES
 
 
 class BeamMoeCfg(ctypes.Structure):
@@ -82,14 +84,15 @@ def lib() -> ctypes.CDLL:
     L.beam_moe_permute.argtypes = [cfgp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
     L.beam_moe_experts.argtypes = [cfgp, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32,
                                    vp, sz, vp]
+    L.beam_moe_experts_static.argtypes = [cfgp, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp]
     L.beam_moe_combine_norm.argtypes = [cfgp, i32, vp, i32, vp, vp, vp, vp, i32, vp, vp, i32, vp, vp]
     L.beam_moe_pack_weights.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp]
     L.beam_moe_workspace_bytes.argtypes = [cfgp, i32, i32]
     L.beam_moe_workspace_bytes.restype = sz
     L.beam_moe_status_string.argtypes = [i32]
     L.beam_moe_status_string.restype = ctypes.c_char_p
-    for f in ("beam_moe_route", "beam_moe_permute", "beam_moe_experts", "beam_moe_combine_norm",
-              "beam_moe_pack_weights"):
+    for f in ("beam_moe_route", "beam_moe_permute", "beam_moe_experts", "beam_moe_experts_static",
+              "beam_moe_combine_norm", "beam_moe_pack_weights"):
         getattr(L, f).restype = i32
     _lib = L
     return L
@@ -204,6 +207,35 @@ def beam_moe_experts(cfg: LayerCfg, T, x, expert_offsets, row_token, w_gate_up, 
                                 _p(w_down), _p(s_down), _p(y), _dt(y), _p(ws),
                                 0 if ws is None else ws.numel(), _stream(stream))
     _ok("beam_moe_experts", st)
+
+
+def _experts_common(cfg, T, x, expert_offsets, row_token, w_gate_up, w_down, y, x_scale, s_gate_up, s_down):
+    E, H, F, TK = cfg.n_experts, cfg.hidden, cfg.d_ff, T * cfg.topk
+    w_dt = _dt(w_gate_up)
+    _check(x, (T, H), (w_gate_up.dtype,) if w_dt != BEAM_FP8_E4M3 else (torch.uint8, torch.float8_e4m3fn), "x")
+    _check(expert_offsets, (E + 1,), (torch.int32,), "expert_offsets")
+    _check(row_token, (TK,), (torch.int32,), "row_token")
+    _check(w_gate_up, (E, 2 * F, H), (w_gate_up.dtype,), "w_gate_up")
+    _check(w_down, (E, H, F), (w_gate_up.dtype,), "w_down")
+    _check(y, (TK, H), (torch.float32, torch.bfloat16), "y")
+    if w_dt == BEAM_FP8_E4M3:
+        _check(x_scale, (T,), (torch.float32,), "x_scale")
+        _check(s_gate_up, (E, 2 * F), (torch.float32,), "s_gate_up")
+        _check(s_down, (E, H), (torch.float32,), "s_down")
+    return w_dt
+
+
+def beam_moe_experts_static(cfg: LayerCfg, T, x, expert_offsets, row_token, w_gate_up, w_down, y,
+                            x_scale=None, s_gate_up=None, s_down=None, stream=None):
+    """beam_moe_experts working in the library's per-GPU static scratch array
+    (no workspace argument, nothing allocated).  Calls that overlap in time
+    on one GPU race; calls ordered on one stream are safe."""
+    w_dt = _experts_common(cfg, T, x, expert_offsets, row_token, w_gate_up, w_down, y, x_scale,
+                           s_gate_up, s_down)
+    st = lib().beam_moe_experts_static(ctypes.byref(cfg.c()), T, w_dt, _p(x), w_dt, _p(x_scale),
+                                       _p(expert_offsets), _p(row_token), _p(w_gate_up), _p(s_gate_up),
+                                       _p(w_down), _p(s_down), _p(y), _dt(y), _stream(stream))
+    _ok("beam_moe_experts_static", st)
 
 
 def beam_moe_combine_norm(cfg: LayerCfg, y, pair_row, topk_w, h, x_next, gamma_post, gamma_pre, n,

@@ -4,7 +4,15 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "kernels.h"
+
+// Workspace of beam_moe_experts_static: one copy of this array per GPU,
+// loaded with the library's device code and held until the process ends.
+// In host code the name is only a stand-in: kernels get the per-device
+// address that hipGetSymbolAddress returns (static_scratch below).
+static __device__ __align__(256) uint8_t scratch[BEAM_MOE_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -47,6 +55,85 @@ size_t route_ws(const beam_moe_cfg* c, int T) {
 
 beam::WKind wkind(beam_dtype d) {
     return d == BEAM_BF16 ? beam::W_BF16 : (d == BEAM_FP8_E4M3 ? beam::W_FP8 : beam::W_F32);
+}
+
+// Checks of beam_moe_experts that do not concern the workspace; fills `a`
+// (all but a.ws) and the workspace bytes the call needs.
+beam_status experts_prepare(const beam_moe_cfg* cfg, int32_t T, beam_dtype w_dtype, const void* x,
+                            beam_dtype x_dtype, const float* x_scale, const int32_t* expert_offsets,
+                            const int32_t* row_token, const void* w_gate_up, const float* s_gate_up,
+                            const void* w_down, const float* s_down, void* y, beam_dtype y_dtype,
+                            beam::ExpertsArgs& a, size_t& need) {
+    beam_status st = check_cfg(cfg);
+    if (st != BEAM_OK) return st;
+    if (T < 0 || T > kMaxT) return BEAM_ERR_INVALID_ARG;
+    if (!valid_dtype(w_dtype) || !valid_dtype(x_dtype) || !valid_dtype(y_dtype))
+        return BEAM_ERR_INVALID_ARG;
+    if (x_dtype != w_dtype) return BEAM_ERR_INVALID_ARG;
+    if (y_dtype == BEAM_FP8_E4M3) return BEAM_ERR_INVALID_ARG;
+    if (w_dtype == BEAM_FP8_E4M3 && (cfg->hidden % 256 != 0 || cfg->d_ff % 256 != 0))
+        return BEAM_ERR_UNSUPPORTED;
+    if (T == 0) return BEAM_OK;
+    if (!x || !expert_offsets || !row_token || !w_gate_up || !w_down || !y) return BEAM_ERR_INVALID_ARG;
+    if (w_dtype == BEAM_FP8_E4M3 && (!x_scale || !s_gate_up || !s_down)) return BEAM_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(y))
+        return BEAM_ERR_INVALID_ARG;
+    if (w_dtype == BEAM_FP8_E4M3 && (!aligned16(s_gate_up) || !aligned16(s_down)))
+        return BEAM_ERR_INVALID_ARG;
+    const beam::WKind wk = wkind(w_dtype);
+    need = beam::experts_ws_bytes(T, cfg->topk, cfg->n_experts, cfg->hidden, cfg->d_ff, wk);
+    a.T = T;
+    a.K = cfg->topk;
+    a.E = cfg->n_experts;
+    a.H = cfg->hidden;
+    a.F = cfg->d_ff;
+    a.w = wk;
+    a.x = x;
+    a.xscale = x_scale;
+    a.offsets = expert_offsets;
+    a.row_token = row_token;
+    a.wgu = w_gate_up;
+    a.sgu = s_gate_up;
+    a.wd = w_down;
+    a.sd = s_down;
+    a.y = y;
+    a.y_bf16 = y_dtype == BEAM_BF16;
+    return BEAM_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device `stream` belongs to, looked up
+// once per device with that device current.
+hipError_t static_scratch(hipStream_t stream, void** out) {
+    int cur = 0;
+    hipError_t err = hipGetDevice(&cur);
+    if (err != hipSuccess) return err;
+    int dev = cur;
+    if (stream) {
+        hipDevice_t d = 0;
+        err = hipStreamGetDevice(stream, &d);
+        if (err != hipSuccess) return err;
+        dev = (int)d;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        if (dev != cur && (err = hipSetDevice(dev)) != hipSuccess) return err;
+        void* p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (err == hipSuccess) err = e2;
+        }
+        if (err != hipSuccess) return err;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 }  // namespace
@@ -147,45 +234,33 @@ beam_status beam_moe_experts(const beam_moe_cfg* cfg, int32_t T, beam_dtype w_dt
                              const int32_t* row_token, const void* w_gate_up, const float* s_gate_up,
                              const void* w_down, const float* s_down, void* y, beam_dtype y_dtype,
                              void* ws, size_t ws_bytes, void* stream) {
-    beam_status st = check_cfg(cfg);
-    if (st != BEAM_OK) return st;
-    if (T < 0 || T > kMaxT) return BEAM_ERR_INVALID_ARG;
-    if (!valid_dtype(w_dtype) || !valid_dtype(x_dtype) || !valid_dtype(y_dtype))
-        return BEAM_ERR_INVALID_ARG;
-    if (x_dtype != w_dtype) return BEAM_ERR_INVALID_ARG;
-    if (y_dtype == BEAM_FP8_E4M3) return BEAM_ERR_INVALID_ARG;
-    if (w_dtype == BEAM_FP8_E4M3 && (cfg->hidden % 256 != 0 || cfg->d_ff % 256 != 0))
-        return BEAM_ERR_UNSUPPORTED;
-    if (T == 0) return BEAM_OK;
-    if (!x || !expert_offsets || !row_token || !w_gate_up || !w_down || !y) return BEAM_ERR_INVALID_ARG;
-    if (w_dtype == BEAM_FP8_E4M3 && (!x_scale || !s_gate_up || !s_down)) return BEAM_ERR_INVALID_ARG;
-    if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(y))
-        return BEAM_ERR_INVALID_ARG;
-    if (w_dtype == BEAM_FP8_E4M3 && (!aligned16(s_gate_up) || !aligned16(s_down)))
-        return BEAM_ERR_INVALID_ARG;
-    const beam::WKind wk = wkind(w_dtype);
-    const size_t need = beam::experts_ws_bytes(T, cfg->topk, cfg->n_experts, cfg->hidden, cfg->d_ff, wk);
-    if (!ws || ws_bytes < need || !aligned16(ws)) return BEAM_ERR_WORKSPACE;
     beam::ExpertsArgs a{};
-    a.T = T;
-    a.K = cfg->topk;
-    a.E = cfg->n_experts;
-    a.H = cfg->hidden;
-    a.F = cfg->d_ff;
-    a.w = wk;
-    a.x = x;
-    a.xscale = x_scale;
-    a.offsets = expert_offsets;
-    a.row_token = row_token;
-    a.wgu = w_gate_up;
-    a.sgu = s_gate_up;
-    a.wd = w_down;
-    a.sd = s_down;
-    a.y = y;
-    a.y_bf16 = y_dtype == BEAM_BF16;
+    size_t need = 0;
+    const beam_status st = experts_prepare(cfg, T, w_dtype, x, x_dtype, x_scale, expert_offsets, row_token,
+                                           w_gate_up, s_gate_up, w_down, s_down, y, y_dtype, a, need);
+    if (st != BEAM_OK || T == 0) return st;
+    if (!ws || ws_bytes < need || !aligned16(ws)) return BEAM_ERR_WORKSPACE;
     a.ws = ws;
     return beam::launch_experts(a, static_cast<hipStream_t>(stream)) == hipSuccess ? BEAM_OK
                                                                                     : BEAM_ERR_HIP;
+}
+
+beam_status beam_moe_experts_static(const beam_moe_cfg* cfg, int32_t T, beam_dtype w_dtype,
+                                    const void* x, beam_dtype x_dtype, const float* x_scale,
+                                    const int32_t* expert_offsets, const int32_t* row_token,
+                                    const void* w_gate_up, const float* s_gate_up, const void* w_down,
+                                    const float* s_down, void* y, beam_dtype y_dtype, void* stream) {
+    beam::ExpertsArgs a{};
+    size_t need = 0;
+    const beam_status st = experts_prepare(cfg, T, w_dtype, x, x_dtype, x_scale, expert_offsets, row_token,
+                                           w_gate_up, s_gate_up, w_down, s_down, y, y_dtype, a, need);
+    if (st != BEAM_OK || T == 0) return st;
+    if (need > BEAM_MOE_STATIC_SCRATCH_BYTES) return BEAM_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* scr = nullptr;
+    if (static_scratch(s, &scr) != hipSuccess) return BEAM_ERR_HIP;
+    a.ws = scr;
+    return beam::launch_experts(a, s) == hipSuccess ? BEAM_OK : BEAM_ERR_HIP;
 }
 
 beam_status beam_moe_pack_weights(const beam_moe_cfg* cfg, int32_t n_experts, beam_dtype w_dtype,

@@ -161,6 +161,36 @@ beam_status beam_moe_experts(const beam_moe_cfg* cfg, int32_t T, beam_dtype w_dt
                              void* y, beam_dtype y_dtype,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of the per-GPU device array beam_moe_experts_static works in. */
+#define BEAM_MOE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * beam_moe_experts_static -- beam_moe_experts without a caller workspace,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).
+ *
+ * Arguments, layouts and results are those of beam_moe_experts minus
+ * ws / ws_bytes; it launches the same kernels.  Its workspace is a
+ * file-scope device array of BEAM_MOE_STATIC_SCRATCH_BYTES (64 MiB) that
+ * every GPU the library runs on holds until the process ends; the first
+ * call on a device looks up that device's copy (no allocation by this
+ * library, no host synchronisation).  Nothing in it has to start at zero:
+ * each call writes every part of it that it reads.
+ *   - Returns BEAM_ERR_UNSUPPORTED, enqueuing nothing, when the experts
+ *     step needs more workspace than that (at the Beam shape: more than
+ *     about 1,600 tokens with bf16 experts, about 540 with fp8 experts).
+ *   - All calls on one GPU share the array: calls that overlap in time on
+ *     one GPU (different streams, threads or graphs running concurrently)
+ *     race and corrupt each other's results.  Calls ordered on one stream
+ *     are safe.
+ */
+beam_status beam_moe_experts_static(const beam_moe_cfg* cfg, int32_t T, beam_dtype w_dtype,
+                                    const void* x, beam_dtype x_dtype, const float* x_scale,
+                                    const int32_t* expert_offsets, const int32_t* row_token,
+                                    const void* w_gate_up, const float* s_gate_up,
+                                    const void* w_down, const float* s_down,
+                                    void* y, beam_dtype y_dtype, void* stream);
+
 /*
  * beam_moe_combine_norm -- weighted combine + sandwich-norm boundary.
  * (TokenSpeed blog, "MNNVL all-reduce and SandwichNorm fusion": post-norm,

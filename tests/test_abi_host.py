@@ -164,3 +164,17 @@ def test_pack_argument_checks(L):
     assert f(pb=FAKE * 4096 + 4096) == 1      # outputs overlap each other
     assert L.beam_moe_pack_weights(ctypes.byref(_cfg(d_ff=384)), 1, 2, FAKE, FAKE * 1024, FAKE * 4096,
                                    FAKE * 8192, None) == 2   # fp8 needs d_ff % 256 == 0
+
+
+def test_experts_static_checks(L):
+    c = _cfg()
+    f = lambda T=8, x_dt=1, y_dt=0, x=FAKE: L.beam_moe_experts_static(
+        ctypes.byref(c), T, 1, x, x_dt, None, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, y_dt, None)
+    assert f(T=0, x=None) == 0                 # nothing to do
+    assert f(x_dt=0) == 1                      # same argument checks as beam_moe_experts
+    assert f(y_dt=2) == 1
+    assert f(x=None) == 1
+    # the Beam shape at T = 4096 needs more than the 64 MiB static scratch:
+    # rejected before anything is enqueued
+    assert L.beam_moe_workspace_bytes(ctypes.byref(c), 4096, 1) > beam.STATIC_SCRATCH_BYTES
+    assert f(T=4096) == 2
