@@ -20,6 +20,8 @@
 // bytes [64 s + 16 g, +16) of its row for piece s, the same k bytes the
 // packed A fragment holds.  bf16: MFMA step s uses piece s.  fp8: MFMA step
 // t uses pieces 2t and 2t+1 (32 bytes = the lane's 32 k values).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -48,10 +50,11 @@ __global__ __launch_bounds__(256) void beam_build_items(const int32_t* __restric
     const int nch = (cnt + MC - 1) / MC;
     int total;
     const int first = block_exclusive_scan(nch, tmp, &total);
-    // .w = 1 when the expert has more than one item: its weights are then
-    // read by several workgroups and should stay cacheable
+    // .w = (index of the item within its expert << 16) | items of the expert;
+    // an expert with more than one item has its weights read by several
+    // workgroups, which should then keep them cacheable
     for (int c = 0; c < nch; ++c)
-        items[first + c] = make_int4(e, offsets[e] + c * MC, min(MC, cnt - c * MC), nch > 1 ? 1 : 0);
+        items[first + c] = make_int4(e, offsets[e] + c * MC, min(MC, cnt - c * MC), (c << 16) | nch);
     if (e == 0) *n_items = total;
 }
 
@@ -97,6 +100,59 @@ struct GemmParams {
 
 template <int V> struct IC { static constexpr int value = V; };
 
+// GEMM1 epilogue of 4 a-columns [f, f+4) of one row: lane holds the gate
+// and up accumulators of weight rows f + i (fp8: scaled back to real units).
+template <int KIND>
+BEAM_DEV void store_swiglu(const GemmParams& p, int e, int f, size_t row, int tok, const f32x4& accg,
+                           const f32x4& accu) {
+    float gv[4], uv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { gv[i] = accg[i]; uv[i] = accu[i]; }
+    if constexpr (KIND == W_FP8) {
+        const int nrows_w = 2 * p.F;
+        const float sx = p.act_scale[tok];
+        const float4 sg = *reinterpret_cast<const float4*>(p.wscale + (size_t)e * nrows_w + f);
+        const float4 su = *reinterpret_cast<const float4*>(p.wscale + (size_t)e * nrows_w + p.F + f);
+        gv[0] *= sx * sg.x; gv[1] *= sx * sg.y; gv[2] *= sx * sg.z; gv[3] *= sx * sg.w;
+        uv[0] *= sx * su.x; uv[1] *= sx * su.y; uv[2] *= sx * su.z; uv[3] *= sx * su.w;
+        float4 av;
+        av.x = silu_f32(gv[0]) * uv[0];
+        av.y = silu_f32(gv[1]) * uv[1];
+        av.z = silu_f32(gv[2]) * uv[2];
+        av.w = silu_f32(gv[3]) * uv[3];
+        *reinterpret_cast<float4*>(static_cast<float*>(p.out) + row * p.F + f) = av;
+    } else {
+        uint16_t hb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16(silu_f32(gv[i]) * uv[i]);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + row * p.F + f) =
+            make_uint2(hb[0] | (uint32_t(hb[1]) << 16), hb[2] | (uint32_t(hb[3]) << 16));
+    }
+}
+
+// GEMM2 epilogue of 4 output columns [o, o+4) of one row.
+template <int KIND>
+BEAM_DEV void store_out(const GemmParams& p, int e, int o, size_t row, const f32x4& acc) {
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = acc[i];
+    if constexpr (KIND == W_FP8) {
+        const float sa = p.act_scale[row];
+        const float4 sw = *reinterpret_cast<const float4*>(p.wscale + (size_t)e * p.H + o);
+        v[0] *= sa * sw.x; v[1] *= sa * sw.y; v[2] *= sa * sw.z; v[3] *= sa * sw.w;
+    }
+    if (p.out_bf16) {
+        uint16_t hb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16(v[i]);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + row * p.H + o) =
+            make_uint2(hb[0] | (uint32_t(hb[1]) << 16), hb[2] | (uint32_t(hb[3]) << 16));
+    } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(p.out) + row * p.H + o) =
+            make_float4(v[0], v[1], v[2], v[3]);
+    }
+}
+
 // Epilogue for one 16-column block: lane holds D[4g+i][r] = weight row
 // (a0/a1 + 4g + i) x item row `row`.  GEMM1 applies SwiGLU (and the fp8
 // scales) and writes a; GEMM2 writes y.
@@ -104,54 +160,11 @@ template <int KIND, bool G1>
 BEAM_DEV void store_block(const GemmParams& p, int e, int a0, int a1, size_t row, int tok,
                           const f32x4& acc0, const f32x4& acc1) {
     const int g = (threadIdx.x & 63) >> 4;
-    const int nrows_w = G1 ? 2 * p.F : p.H;
     if constexpr (G1) {
-        const int f = a0 + 4 * g;
-        float gv[4], uv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { gv[i] = acc0[i]; uv[i] = acc1[i]; }
-        if constexpr (KIND == W_FP8) {
-            const float sx = p.act_scale[tok];
-            const float4 sg = *reinterpret_cast<const float4*>(p.wscale + (size_t)e * nrows_w + f);
-            const float4 su = *reinterpret_cast<const float4*>(p.wscale + (size_t)e * nrows_w + p.F + f);
-            gv[0] *= sx * sg.x; gv[1] *= sx * sg.y; gv[2] *= sx * sg.z; gv[3] *= sx * sg.w;
-            uv[0] *= sx * su.x; uv[1] *= sx * su.y; uv[2] *= sx * su.z; uv[3] *= sx * su.w;
-            float4 av;
-            av.x = silu_f32(gv[0]) * uv[0];
-            av.y = silu_f32(gv[1]) * uv[1];
-            av.z = silu_f32(gv[2]) * uv[2];
-            av.w = silu_f32(gv[3]) * uv[3];
-            *reinterpret_cast<float4*>(static_cast<float*>(p.out) + row * p.F + f) = av;
-        } else {
-            uint16_t hb[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16(silu_f32(gv[i]) * uv[i]);
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + row * p.F + f) =
-                make_uint2(hb[0] | (uint32_t(hb[1]) << 16), hb[2] | (uint32_t(hb[3]) << 16));
-        }
+        store_swiglu<KIND>(p, e, a0 + 4 * g, row, tok, acc0, acc1);
     } else {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int o = (t == 0 ? a0 : a1) + 4 * g;
-            float v[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = (t == 0 ? acc0[i] : acc1[i]);
-            if constexpr (KIND == W_FP8) {
-                const float sa = p.act_scale[row];
-                const float4 sw = *reinterpret_cast<const float4*>(p.wscale + (size_t)e * nrows_w + o);
-                v[0] *= sa * sw.x; v[1] *= sa * sw.y; v[2] *= sa * sw.z; v[3] *= sa * sw.w;
-            }
-            if (p.out_bf16) {
-                uint16_t hb[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16(v[i]);
-                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + row * p.H + o) =
-                    make_uint2(hb[0] | (uint32_t(hb[1]) << 16), hb[2] | (uint32_t(hb[3]) << 16));
-            } else {
-                *reinterpret_cast<float4*>(static_cast<float*>(p.out) + row * p.H + o) =
-                    make_float4(v[0], v[1], v[2], v[3]);
-            }
-        }
+        store_out<KIND>(p, e, a0 + 4 * g, row, acc0);
+        store_out<KIND>(p, e, a1 + 4 * g, row, acc1);
     }
 }
 
@@ -359,8 +372,192 @@ __global__ __launch_bounds__(256, KIND == W_BF16 ? 2 : 1) void beam_expert_gemm_
     const int4 it = p.items[item];
     // weights read once (single-item expert): non-temporal; shared by the
     // expert's other items: plain loads that stay in L2
-    if (it.w == 0) dispatch_lds<KIND, G1, true>(p, it, tile, bs);
+    if ((it.w & 0xFFFF) == 1) dispatch_lds<KIND, G1, true>(p, it, tile, bs);
     else dispatch_lds<KIND, G1, false>(p, it, tile, bs);
+}
+
+// ---- wide tiles for large items: each wave owns FOUR 16-row weight tiles
+// (GEMM1: 32 gate rows and the 32 matching up rows; GEMM2: 64 output rows),
+// so a workgroup covers 256 weight rows x up to 128 item rows and every
+// activation fragment read from LDS feeds four MFMAs instead of two.  The
+// 4 x NB accumulator tiles live in registers (AGPRs), one wave per SIMD.
+template <int KIND, bool G1>
+BEAM_DEV void wide_rows(const GemmParams& p, int e, int tile, int (&a)[4], const uint8_t* (&pa)[4]) {
+    constexpr int ES = (KIND == W_BF16) ? 2 : 1;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kbytes = (G1 ? p.H : p.F) * ES;
+    const int nrows_w = G1 ? 2 * p.F : p.H;
+    if constexpr (G1) {
+        const int f0 = tile * 128 + wave * 32;
+        a[0] = f0; a[1] = f0 + 16; a[2] = p.F + f0; a[3] = p.F + f0 + 16;
+    } else {
+        const int o0 = tile * 256 + wave * 64;
+        a[0] = o0; a[1] = o0 + 16; a[2] = o0 + 32; a[3] = o0 + 48;
+    }
+    const uint8_t* We = p.W + (size_t)e * nrows_w * kbytes;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pa[j] = We + (size_t)(a[j] >> 4) * 16 * kbytes + lane * 16;
+}
+
+// 32 bytes at p and p + 1024 (two pieces of a packed tile, or of an LDS
+// row) as the 8-register operand of the fp8 MFMA
+BEAM_DEV i32x8 pair8(uint4 lo, uint4 hi) {
+    return __builtin_shufflevector(__builtin_bit_cast(i32x4v, lo), __builtin_bit_cast(i32x4v, hi), 0, 1, 2, 3,
+                                   4, 5, 6, 7);
+}
+
+template <int KIND, bool G1, int NB, bool NT>
+BEAM_DEV void gemm_item_wide(const GemmParams& p, int e, int row0, int rows, int tile,
+                             uint4 (*bs)[kLdsRows * 16]) {
+    constexpr int ES = (KIND == W_BF16) ? 2 : 1;
+    constexpr int NS = (KIND == W_BF16) ? 4 : 2;   // MFMA steps per 256-byte K iteration
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int kbytes = (G1 ? p.H : p.F) * ES;
+    const int nk = kbytes / kKIterBytes;
+    int a[4];
+    const uint8_t* pa[4];
+    wide_rows<KIND, G1>(p, e, tile, a, pa);
+
+    // loader role: thread t copies chunk c = t % 16 of rows t/16 + 16 i
+    const int lc = threadIdx.x & 15, lr = threadIdx.x >> 4;
+    int srow[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        // padding rows of a partial item load a real row (the item's first):
+        // an output row depends only on its own input row, and padding
+        // rows are never stored
+        const int rr = lr + 16 * i < rows ? lr + 16 * i : 0;
+        srow[i] = G1 ? p.row_token[row0 + rr] : row0 + rr;
+    }
+    const uint8_t* act = p.act + 16 * lc;
+    uint4 stage[NB];
+    auto gload = [&](int k) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) stage[i] = ld16(act + (size_t)srow[i] * kbytes + k);
+    };
+    auto swrite = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) bs[buf][lds_pos(lr + 16 * i, lc)] = stage[i];
+    };
+    auto wload = [&](int j, int q, int k) -> uint4 {
+        if constexpr (NT) return ld16_nt(pa[j] + (size_t)k * 16 + 1024 * q);
+        else return ld16(pa[j] + (size_t)k * 16 + 1024 * q);
+    };
+
+    f32x4 acc[4][NB];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[j][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // One set of weight fragments, one register group per MFMA step; the
+    // group of step st is reloaded for the next K iteration as soon as the
+    // step's last MFMA has issued (one iteration of latency to hide).
+    using WFrag = typename std::conditional<KIND == W_BF16, uint4, i32x8>::type;
+    WFrag wa[4][NS];
+    auto aload_step = [&](int st, int k) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (KIND == W_BF16) wa[j][st] = wload(j, st, k);
+            else wa[j][st] = pair8(wload(j, 2 * st, k), wload(j, 2 * st + 1, k));
+        }
+    };
+    gload(0);
+#pragma unroll
+    for (int st = 0; st < NS; ++st) aload_step(st, 0);
+    swrite(0);
+    __syncthreads();
+    // One straight-line body for both LDS buffers (runtime buffer index):
+    // the weight registers are reloaded in place, and with no branches in
+    // the body the scheduling barriers keep every MFMA step ahead of the
+    // reload of its own weight registers.  The last iteration reloads its
+    // own K slice (in bounds, never used).
+    for (int kit = 0; kit < nk; ++kit) {
+        const int cur = kit & 1;
+        const int knext = (kit + 1 < nk ? kit + 1 : kit) * kKIterBytes;
+        gload(knext);
+        const uint4* bcur = bs[cur];
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                if constexpr (KIND == W_BF16) {
+                    const uint4 xb = bcur[lds_pos(nb * 16 + r, 4 * st + g)];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[j][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, wa[j][st]), __builtin_bit_cast(bf16x8, xb), acc[j][nb],
+                            0, 0, 0);
+                } else {
+                    const i32x8 bv = pair8(bcur[lds_pos(nb * 16 + r, 4 * (2 * st) + g)],
+                                           bcur[lds_pos(nb * 16 + r, 4 * (2 * st + 1) + g)]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        // formats 0/0 = e4m3 x e4m3; block scales 127 = 2^0 (unscaled)
+                        acc[j][nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa[j][st], bv, acc[j][nb],
+                                                                                      0, 0, 0, 127, 0, 127);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            aload_step(st, knext);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        swrite(cur ^ 1);
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int c = nb * 16 + r;
+        if (c < rows) {
+            const size_t row = (size_t)row0 + c;
+            if constexpr (G1) {
+                const int tok = p.row_token[row0 + c];
+                store_swiglu<KIND>(p, e, a[0] + 4 * g, row, tok, acc[0][nb], acc[2][nb]);
+                store_swiglu<KIND>(p, e, a[1] + 4 * g, row, tok, acc[1][nb], acc[3][nb]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) store_out<KIND>(p, e, a[j] + 4 * g, row, acc[j][nb]);
+            }
+        }
+    }
+}
+
+template <int KIND, bool G1, bool NT>
+BEAM_DEV void dispatch_wide(const GemmParams& p, int4 it, int tile, uint4 (*bs)[kLdsRows * 16]) {
+    if (it.z <= 16)
+        gemm_item_wide<KIND, G1, 1, NT>(p, it.x, it.y, it.z, tile, bs);
+    else if (it.z <= 32)
+        gemm_item_wide<KIND, G1, 2, NT>(p, it.x, it.y, it.z, tile, bs);
+    else if (it.z <= 64)
+        gemm_item_wide<KIND, G1, 4, NT>(p, it.x, it.y, it.z, tile, bs);
+    else
+        gemm_item_wide<KIND, G1, 8, NT>(p, it.x, it.y, it.z, tile, bs);
+}
+
+// Block -> (item, N-tile).  Work units are ordered expert by expert, N-tile
+// by N-tile, item by item, so the items of one expert that share an N-tile
+// of weights are neighbours.  Workgroups go to the 8 XCDs round-robin
+// (block b runs on XCD b % 8), so each XCD is given one contiguous range of
+// units: neighbours share its L2 and each weight tile is fetched once for
+// all the items of its expert.
+template <int KIND, bool G1>
+__global__ __launch_bounds__(256, 1) void beam_expert_gemm_wide(GemmParams p) {
+    __shared__ uint4 bs[2][kLdsRows * 16];
+    const int total = *p.n_items * p.n_tiles;
+    const int per_xcd = (total + 7) >> 3;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    if (slot >= per_xcd) return;
+    const int j = xcd * per_xcd + slot;
+    if (j >= total) return;
+    const int4 any = p.items[j / p.n_tiles];          // an item of the unit's expert
+    const int cnt = any.w & 0xFFFF;
+    const int first = j / p.n_tiles - (any.w >> 16);  // the expert's first item
+    const int local = j - first * p.n_tiles;          // = tile * cnt + item within the expert
+    const int tile = local / cnt;
+    const int4 it = p.items[first + (local - tile * cnt)];
+    if (cnt == 1) dispatch_wide<KIND, G1, true>(p, it, tile, bs);
+    else dispatch_wide<KIND, G1, false>(p, it, tile, bs);
 }
 
 // Per-row e4m3 re-quantisation of the fp32 SwiGLU output (fp8 path).
@@ -474,12 +671,37 @@ size_t experts_ws_bytes(int T, int K, int E, int H, int F, WKind w) {
     return carve(nullptr, T, K, E, F, w).bytes;
 }
 
+// Kernel choice by the mean rows per expert, T*K/E:
+//   T <= 16:   one 16-row item per touched expert, weights straight into
+//              registers (beam_expert_gemm_direct);
+//   < 256:     mostly one 128-row item per expert, so each weight byte is
+//              streamed once: two 16-row weight tiles per wave, two waves
+//              per SIMD for more bytes in flight (beam_expert_gemm_lds);
+//   >= 256:    several items per expert sharing each weight tile through
+//              L2: four weight tiles per wave, XCD-grouped work order
+//              (beam_expert_gemm_wide), grid rounded to whole XCD rounds.
+enum GemmPath { PATH_DIRECT, PATH_LDS, PATH_WIDE };
+
+static GemmPath gemm_path(int T, int K, int E) {
+    if (T <= 16) return PATH_DIRECT;
+    return (long long)T * K >= 256LL * E ? PATH_WIDE : PATH_LDS;
+}
+
 template <int KIND, bool G1>
-static void launch_gemm(const GemmParams& p, int n_blocks, int mc, hipStream_t st) {
-    if (mc == 16)
-        hipLaunchKernelGGL((beam_expert_gemm_direct<KIND, G1>), dim3(n_blocks), dim3(256), 0, st, p);
+static void launch_gemm(GemmParams p, int n_items_max, GemmPath path, hipStream_t st) {
+    const int H = p.H, F = p.F;
+    if (path == PATH_WIDE) {
+        p.n_tiles = G1 ? F / 128 : H / 256;
+        const int blocks = (n_items_max * p.n_tiles + 7) / 8 * 8;
+        hipLaunchKernelGGL((beam_expert_gemm_wide<KIND, G1>), dim3(blocks), dim3(256), 0, st, p);
+        return;
+    }
+    p.n_tiles = G1 ? F / 64 : H / 128;
+    if (path == PATH_DIRECT)
+        hipLaunchKernelGGL((beam_expert_gemm_direct<KIND, G1>), dim3(n_items_max * p.n_tiles), dim3(256), 0,
+                           st, p);
     else
-        hipLaunchKernelGGL((beam_expert_gemm_lds<KIND, G1>), dim3(n_blocks), dim3(256), 0, st, p);
+        hipLaunchKernelGGL((beam_expert_gemm_lds<KIND, G1>), dim3(n_items_max * p.n_tiles), dim3(256), 0, st, p);
 }
 
 hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st) {
@@ -494,6 +716,7 @@ hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st) {
     }
     const int mc = rows_per_item(a.T);
     const int n_items_max = (int)max_items(a.T, a.K, a.E);
+    const GemmPath path = gemm_path(a.T, a.K, a.E);
     hipLaunchKernelGGL(beam_build_items, dim3(1), dim3(256), 0, st, a.offsets, a.E, mc, ws.items,
                        ws.n_items);
 
@@ -504,7 +727,6 @@ hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st) {
     p.F = a.F;
 
     // GEMM1 + SwiGLU
-    p.n_tiles = a.F / 64;
     p.act = static_cast<const uint8_t*>(a.x);
     p.row_token = a.row_token;
     p.act_scale = a.xscale;
@@ -513,12 +735,11 @@ hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st) {
     p.out = ws.a;
     p.out_bf16 = false;
     if (a.w == W_BF16)
-        launch_gemm<W_BF16, true>(p, n_items_max * p.n_tiles, mc, st);
+        launch_gemm<W_BF16, true>(p, n_items_max, path, st);
     else
-        launch_gemm<W_FP8, true>(p, n_items_max * p.n_tiles, mc, st);
+        launch_gemm<W_FP8, true>(p, n_items_max, path, st);
 
     // GEMM2
-    p.n_tiles = a.H / 128;
     p.row_token = nullptr;
     p.W = static_cast<const uint8_t*>(a.wd);
     p.wscale = a.sd;
@@ -529,11 +750,11 @@ hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st) {
                            a.offsets, a.E, a.F, ws.aq, ws.ascale);
         p.act = ws.aq;
         p.act_scale = ws.ascale;
-        launch_gemm<W_FP8, false>(p, n_items_max * p.n_tiles, mc, st);
+        launch_gemm<W_FP8, false>(p, n_items_max, path, st);
     } else {
         p.act = static_cast<const uint8_t*>(ws.a);
         p.act_scale = nullptr;
-        launch_gemm<W_BF16, false>(p, n_items_max * p.n_tiles, mc, st);
+        launch_gemm<W_BF16, false>(p, n_items_max, path, st);
     }
     return hipGetLastError();
 }

@@ -1,8 +1,8 @@
 """GPU parity of the whole layer (route -> permute -> experts ->
 combine_norm, in the launch configuration the bench times) against the CPU
 oracle, for every workload: the tiny all-fp32 layer in full, and the Beam
-shapes (T = 8, 64 skewed, 2048 prefill, 16384 with fp8 experts) with all
-256 experts resident.
+shapes (T = 8, 64 skewed, 2048 prefill, 16384 with bf16 and with fp8
+experts) with all 256 experts resident.
 
 Per workload:
   * routing of every token (ids exact outside near-ties, weights 1e-5);
@@ -310,6 +310,11 @@ def test_layer_prefill_t2048():
 
 def test_layer_graph_replay_prefill_t2048():
     run_graph_replay("prefill_t2048")
+
+
+@pytest.mark.timeout(400)
+def test_layer_prefill_bf16_t16384():
+    run_layer("prefill_bf16_t16384", 32)
 
 
 @pytest.mark.timeout(400)

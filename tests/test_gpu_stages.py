@@ -197,13 +197,19 @@ def _run_experts_stage(wl, T, ids_np, y_dtype):
 
 @pytest.mark.parametrize("w_dtype,y_dtype,T,skew", [
     ("bf16", torch.float32, 5, 0.0),      # <= 16 tokens: one row block per item
-    ("bf16", torch.float32, 300, 0.5),    # up to 64 rows per item, ragged tails, 2+ items per expert
+    ("bf16", torch.float32, 300, 0.5),    # 128-row items, ragged tails, 2+ items per expert
     ("bf16", torch.bfloat16, 300, 0.5),
     ("bf16", torch.float32, 37, 3.0),     # heavy skew: empty experts
     ("fp8", torch.float32, 5, 0.0),
     ("fp8", torch.float32, 300, 0.5),
     ("fp8", torch.bfloat16, 300, 0.5),
     ("f32", torch.float32, 33, 0.5),
+    # >= 256 rows per expert on average (T*K >= 256*E): the wide-tile kernel
+    # with several 128-row items per expert and ragged last items
+    ("bf16", torch.float32, 1500, 0.5),
+    ("bf16", torch.bfloat16, 1100, 2.0),
+    ("fp8", torch.float32, 1500, 0.5),
+    ("fp8", torch.bfloat16, 1100, 2.0),
 ])
 def test_experts_parity(w_dtype, y_dtype, T, skew):
     say(f"experts {w_dtype} y={y_dtype} T={T} skew={skew}")
@@ -219,7 +225,7 @@ def test_experts_parity(w_dtype, y_dtype, T, skew):
 
 
 def test_experts_every_token_on_one_expert():
-    say("experts: 150 rows on one expert (3 items of <=64 rows)")
+    say("experts: 150 rows on one expert (items of 128 + 22 rows)")
     wl = _stage_wl("bf16", H=512, F=256)
     rng = np.random.default_rng(12)
     T, E, K = 150, wl.n_experts, wl.topk
