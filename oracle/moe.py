@@ -39,6 +39,8 @@ __all__ = [
     "router_logits", "sigmoid", "silu", "Route", "route_token", "route",
     "permutation", "expert_ffn", "expert_ffn_w8a8", "combine", "rmsnorm",
     "norm_boundary", "layer_tokens", "E4M3_MAX",
+    "E2M1_MAX", "MX_BLOCK", "e2m1_decode", "e2m1_round", "e2m1_encode", "e8m0_decode",
+    "quantize_mx_fp4", "unpack_fp4", "expert_ffn_w4a4",
 ]
 
 E4M3_MAX = 448.0
@@ -314,6 +316,143 @@ def expert_ffn_w8a8(u, q_gu, s_gu, q_d, s_d):
     return sa[:, None] * s_d[None, :] * (qa @ wd.T)
 
 
+# --------------------------------------------------------------------------
+# 4-bit experts.  The pages' 4-bit checkpoint stores every expert weight as a
+# 4-bit float (E2M1) with an FP8 scale per 16 weights and an FP32 scale per
+# expert ([TS] "NVFP4 and FP8 checkpoints"), and the 4-bit MoE kernel
+# quantises its inputs to 4 bits at run time ([TS] "TensorRT-LLM NVFP4
+# MoE").  This build re-encodes the weights in the OCP microscaling format
+# MXFP4, which the target's matrix cores consume natively: E2M1 elements
+# with one power-of-two (E8M0) scale per block of 32 consecutive elements of
+# a row (OCP Microscaling Formats (MX) specification v1.0).
+# --------------------------------------------------------------------------
+
+E2M1_MAX = 6.0
+MX_BLOCK = 32
+_E2M1_MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def e2m1_decode(codes):
+    """Values of FP4 E2M1 codes (the low 4 bits of each integer).
+
+    Layout: sign bit 3, exponent bits 2..1 with bias 1, mantissa bit 0.
+    Exponent field 0 is subnormal (m * 0.5); otherwise (1 + m/2) * 2^(E-1).
+    There is no infinity or NaN; the largest magnitude is 1.5 * 4 = 6.
+    """
+    c = np.asarray(codes, dtype=np.int64) & 0xF
+    ef = (c >> 1) & 0x3
+    mf = (c & 0x1).astype(np.float64)
+    mag = np.where(ef == 0, mf * 0.5, (1.0 + mf / 2.0) * np.exp2(ef - 1.0))
+    return np.where(c & 0x8, -mag, mag)
+
+
+def e8m0_decode(codes):
+    """Values of E8M0 scale codes: 2^(c - 127); code 255 is NaN."""
+    c = np.asarray(codes, dtype=np.int64) & 0xFF
+    return np.where(c == 255, np.nan, np.exp2(c - 127.0))
+
+
+def e2m1_round(v):
+    """Nearest E2M1 value of each element, ties to the even mantissa,
+    saturating at +-6 (the conversion rule of the MX specification for FP4
+    elements).  NaN stays NaN.
+
+    The non-negative grid is 0, 0.5, 1, 1.5, 2, 3, 4, 6; its spacing is 0.5
+    below 2, 1 in [2, 4) and 2 in [4, 6]."""
+    v = np.asarray(v, dtype=np.float64)
+    out = np.array(v, copy=True)
+    fin = np.isfinite(v)
+    x = np.minimum(np.abs(v[fin]), E2M1_MAX)
+    step = np.where(x < 2.0, 0.5, np.where(x < 4.0, 1.0, 2.0))
+    q = np.round(x / step) * step        # np.round: half to even (in units of step)
+    # a tie at a spacing change (e.g. 1.75 -> 1.5 / 2) is decided by
+    # np.round in the lower spacing; the even mantissa there is correct too
+    out[fin] = np.copysign(np.minimum(q, E2M1_MAX), v[fin])
+    inf = np.isinf(v)
+    out[inf] = np.copysign(E2M1_MAX, v[inf])
+    return out
+
+
+def e2m1_encode(values):
+    """E2M1 codes of values that lie on the grid (uint8, one code per value)."""
+    v = np.asarray(values, dtype=np.float64)
+    mag = np.abs(v)
+    idx = np.searchsorted(_E2M1_MAG, mag)
+    if not np.all(_E2M1_MAG[np.minimum(idx, 7)] == mag):
+        raise ValueError("value not on the E2M1 grid")
+    return (idx | np.where(np.signbit(v), 8, 0)).astype(np.uint8)
+
+
+def quantize_mx_fp4(v):
+    """MX quantisation of each block of 32 consecutive elements (last axis).
+
+    Per block: amax = max |v_i|; shared exponent e = floor(log2(amax)) - 2
+    (2 = the largest exponent of E2M1, so amax / 2^e lies in [4, 8));
+    scale X = 2^e, kept within the E8M0 range [2^-127, 2^127];
+    elements = e2m1_round(v_i / X) (division by a power of two is exact).
+    An all-zero block gets the smallest scale and zero elements.
+    Returns (scale codes uint8 [..., n/32], quantised element values
+    float64 [..., n]) -- the dequantised value is element * 2^(code - 127).
+    """
+    v = np.asarray(v, dtype=np.float64)
+    n = v.shape[-1]
+    if n % MX_BLOCK:
+        raise ValueError("length must be a multiple of 32")
+    blk = v.reshape(v.shape[:-1] + (n // MX_BLOCK, MX_BLOCK))
+    amax = np.max(np.abs(blk), axis=-1)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))    # amax = m * 2^ex, m in [0.5, 1)
+    e = np.where(amax > 0, ex - 1 - 2, -127)
+    e = np.clip(e, -127, 127)
+    q = e2m1_round(blk / np.exp2(e)[..., None])
+    return (e + 127).astype(np.uint8), q.reshape(v.shape)
+
+
+def unpack_fp4(packed):
+    """E2M1 codes of a packed array: byte i holds element 2i in its low
+    nibble and element 2i + 1 in its high nibble."""
+    b = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = b & 0xF
+    out[..., 1::2] = b >> 4
+    return out
+
+
+def expert_ffn_w4a4(u, c_gu, s_gu, c_d, s_d, intermediates=False):
+    """One expert's SwiGLU MLP with MXFP4 weights and activations.
+
+    c_gu [2F,H] / c_d [H,F]: E2M1 codes (one per element); s_gu [2F,H/32] /
+    s_d [H,F/32]: E8M0 codes of the blocks of 32 along each row.  For each
+    row of u (taken in fp32, as stored):
+      (sx, qx) = quantize_mx_fp4(u);  x~ = qx * 2^(sx - 127) per block
+      g = x~ W_g~^T, v = x~ W_u~^T   with W~ = E2M1 value * 2^(s - 127)
+      a = fp32(silu(g) * v);  (sa, qa) = quantize_mx_fp4(a) over all F
+      y = a~ W_d~^T
+    The rounding of a to fp32 before its quantisation is the reading taken
+    for where the intermediate is stored (the run-time activation
+    quantisation reads fp32 values; the decision that picks each code is
+    then taken on the same fp32 value the kernel holds).  The products are
+    exact and their sums are taken in fp64.
+    """
+    u = np.atleast_2d(np.asarray(u, np.float64)).astype(np.float32).astype(np.float64)
+    def deq(c, s):
+        vals = e2m1_decode(c)
+        sc = np.repeat(e8m0_decode(s), MX_BLOCK, axis=-1)
+        return vals * sc
+    wgu = deq(c_gu, s_gu)
+    wd = deq(c_d, s_d)
+    F = wgu.shape[0] // 2
+    sx, qx = quantize_mx_fp4(u)
+    xq = qx * np.repeat(e8m0_decode(sx), MX_BLOCK, axis=-1)
+    gv = xq @ wgu.T
+    a = (silu(gv[:, :F]) * gv[:, F:]).astype(np.float32).astype(np.float64)
+    sa, qa = quantize_mx_fp4(a)
+    aq = qa * np.repeat(e8m0_decode(sa), MX_BLOCK, axis=-1)
+    y = aq @ wd.T
+    if intermediates:
+        return y, {"xq": xq, "g": gv[:, :F], "v": gv[:, F:], "a": a, "aq": aq, "sx": sx, "sa": sa}
+    return y
+
+
 def combine(y, w):
     """Weighted combine m = sum_k w_k y_k of one token's K expert outputs
     ([TS] "TensorRT-LLM NVFP4 MoE": weighted sum per token; [VL] kernel
@@ -353,8 +492,9 @@ def layer_tokens(cfg, x, w_r, bias, expert_weights, h, gamma_post, gamma_pre, n,
     """Whole layer for the listed tokens (default: all).
 
     x, h [T,H]; w_r [E,H]; bias [E]; gammas [H] (numpy, any float dtype).
-    expert_weights(e) returns {"w_gu","w_d"} (float) or
-    {"q_gu","s_gu","q_d","s_d"} (w_dtype "fp8").  rnd is the storage
+    expert_weights(e) returns {"w_gu","w_d"} (float),
+    {"q_gu","s_gu","q_d","s_d"} (w_dtype "fp8") or {"c_gu","s_gu","c_d","s_d"}
+    (w_dtype "mxfp4": E2M1 codes and E8M0 block scales).  rnd is the storage
     rounding of a, p, h', x_next (round_bf16, or round_f32 for the all-fp32
     layer).  ids_override {t: ids} replaces a token's chosen experts (used
     to re-evaluate near-tie tokens with another valid choice).
@@ -385,6 +525,8 @@ def layer_tokens(cfg, x, w_r, bias, expert_weights, h, gamma_post, gamma_pre, n,
                 u = x[tokens[i]]
                 if w_dtype == "fp8":
                     y[i][k] = expert_ffn_w8a8(u, wts["q_gu"], wts["s_gu"], wts["q_d"], wts["s_d"])[0]
+                elif w_dtype == "mxfp4":
+                    y[i][k] = expert_ffn_w4a4(u, wts["c_gu"], wts["s_gu"], wts["c_d"], wts["s_d"])[0]
                 else:
                     y[i][k] = expert_ffn(u, wts["w_gu"], wts["w_d"], round_a=rnd)[0]
     out = {"tokens": tokens, "routes": routes, "logits": logits, "y": [], "m": [],

@@ -71,6 +71,12 @@ WORKLOADS = {
                               seed=1, **_BEAM),
     "prefill_fp8_t16384": Workload("prefill_fp8_t16384", T=16384, n=20, act_dtype="bf16",
                                    w_dtype="fp8", bias_sigma=0.02, seed=1, **_BEAM),
+    # the decode shapes with 4-bit (MXFP4) experts quantised from the same
+    # float weights as the bf16 ones
+    "decode_t8_mxfp4": Workload("decode_t8_mxfp4", T=8, n=20, act_dtype="bf16", w_dtype="mxfp4",
+                                bias_sigma=0.02, seed=1, **_BEAM),
+    "skew_t64_mxfp4": Workload("skew_t64_mxfp4", T=64, n=20, act_dtype="bf16", w_dtype="mxfp4",
+                               bias_sigma=0.02, zipf_s=1.1, seed=1, **_BEAM),
     # the fp8 prefill shape with the bf16 experts of the other Beam workloads:
     # about 512 rows per expert, past the point where bf16 matrix-core
     # throughput rather than HBM bandwidth bounds the expert GEMMs
@@ -78,9 +84,9 @@ WORKLOADS = {
                                     w_dtype="bf16", bias_sigma=0.02, seed=1, **_BEAM),
 }
 # the order the workloads are listed in (index = position in that list; the
-# bf16 16384-token shape was added after the first five)
+# bf16 16384-token shape and the 4-bit decode shapes came after the first five)
 WORKLOAD_ORDER = ["tiny_fp32", "decode_t8", "skew_t64", "prefill_t2048", "prefill_fp8_t16384",
-                  "prefill_bf16_t16384"]
+                  "prefill_bf16_t16384", "decode_t8_mxfp4", "skew_t64_mxfp4"]
 
 
 def _seed(*parts: int) -> int:
@@ -145,13 +151,42 @@ def _quantize_rows_e4m3(w: torch.Tensor):
     return q.view(torch.uint8), s.squeeze(-1).to(torch.float32)
 
 
+_E2M1_GRID = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def _quantize_rows_mxfp4(w: torch.Tensor):
+    """Offline MXFP4 weight format (OCP microscaling): every block of 32
+    consecutive weights of a row shares the power-of-two scale
+    2^(floor(log2(amax)) - 2); each weight becomes the nearest E2M1 value of
+    w / scale (ties to the even code, saturating at 6).  Returns packed codes
+    [rows, cols/2] uint8 (element 2i in the low nibble of byte i) and the
+    E8M0 scale codes [rows, cols/32] uint8.  A checkpoint format step, not
+    part of the layer."""
+    rows, cols = w.shape
+    blk = w.reshape(rows, cols // 32, 32).to(torch.float64)
+    amax = blk.abs().amax(dim=-1)
+    _, ex = torch.frexp(torch.where(amax > 0, amax, torch.ones_like(amax)))
+    e = torch.where(amax > 0, ex.to(torch.int64) - 3, torch.full_like(ex, -127, dtype=torch.int64)).clamp(-127, 127)
+    y = (blk.abs() / torch.exp2(e.to(torch.float64)).unsqueeze(-1)).clamp(max=6.0)
+    grid = torch.tensor(_E2M1_GRID, dtype=torch.float64, device=w.device)
+    mids = (grid[1:] + grid[:-1]) / 2
+    idx = torch.bucketize(y, mids, right=False)            # y <= mid -> lower code
+    tie = (idx < 7) & (y == mids[idx.clamp(max=6)])
+    idx = idx + (tie & (idx % 2 == 1)).to(idx.dtype)       # ties to the even code
+    code = idx | torch.where(blk < 0, 8, 0)
+    code = code.reshape(rows, cols).to(torch.uint8)
+    packed = code[:, 0::2] | (code[:, 1::2] << 4)
+    return packed.contiguous(), (e + 127).to(torch.uint8).contiguous()
+
+
 def make_expert(wl: Workload, e: int, device="cpu"):
     """Weights of expert e.
 
     Returns (w_gate_up [2F,H], w_down [H,F], s_gate_up [2F] | None, s_down [H] | None).
     Rows [0,F) of w_gate_up are the gate projection, rows [F,2F) the up
     projection.  bf16/f32 stacks carry no scales; fp8 stacks are uint8 e4m3
-    codes with one fp32 scale per output row."""
+    codes with one fp32 scale per output row; mxfp4 stacks are packed E2M1
+    codes [2F,H/2] / [H,F/2] with E8M0 scale codes [2F,H/32] / [H,F/32]."""
     H, F = wl.hidden, wl.d_ff
     wg = _randn((F, H), 1.0 / math.sqrt(H), device, wl.seed, _WG, e)
     wu = _randn((F, H), 1.0 / math.sqrt(H), device, wl.seed, _WU, e)
@@ -165,19 +200,27 @@ def make_expert(wl: Workload, e: int, device="cpu"):
         qgu, sgu = _quantize_rows_e4m3(wgu)
         qd, sd = _quantize_rows_e4m3(wd)
         return qgu, qd, sgu, sd
+    if wl.w_dtype == "mxfp4":
+        cgu, sgu = _quantize_rows_mxfp4(wgu)
+        cd, sd = _quantize_rows_mxfp4(wd)
+        return cgu, cd, sgu, sd
     raise ValueError(wl.w_dtype)
 
 
 def make_expert_stacks(wl: Workload, device="cpu"):
     """All E experts stacked: w_gate_up [E,2F,H], w_down [E,H,F] (+ scales for fp8)."""
     E, H, F = wl.n_experts, wl.hidden, wl.d_ff
-    wdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[wl.w_dtype]
-    wgu = torch.empty((E, 2 * F, H), dtype=wdt, device=device)
-    wd = torch.empty((E, H, F), dtype=wdt, device=device)
+    wdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8, "mxfp4": torch.uint8}[wl.w_dtype]
+    cdiv = 2 if wl.w_dtype == "mxfp4" else 1
+    wgu = torch.empty((E, 2 * F, H // cdiv), dtype=wdt, device=device)
+    wd = torch.empty((E, H, F // cdiv), dtype=wdt, device=device)
     sgu = sd = None
     if wl.w_dtype == "fp8":
         sgu = torch.empty((E, 2 * F), dtype=torch.float32, device=device)
         sd = torch.empty((E, H), dtype=torch.float32, device=device)
+    if wl.w_dtype == "mxfp4":
+        sgu = torch.empty((E, 2 * F, H // 32), dtype=torch.uint8, device=device)
+        sd = torch.empty((E, H, F // 32), dtype=torch.uint8, device=device)
     for e in range(E):
         a, b, c, d = make_expert(wl, e, device)
         wgu[e].copy_(a)
