@@ -7,7 +7,8 @@ and all 256 experts' weights resident in HBM.  The headline line is the
 Beam decode shape (T = 8 tokens, bf16 experts); the same JSON line carries
 the other shapes the metric is quoted on (T = 64 with skewed routes,
 T = 2048 prefill, T = 16384 with fp8 experts, and T = 16384 with bf16
-experts) under "configs".  Prints one JSON line.
+experts) and the decode shapes with 4-bit MXFP4 experts (T = 8 and 64)
+under "configs".  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--configs a,b|none]
 
@@ -41,7 +42,8 @@ FP8_MFMA_TFLOPS = 5000.0
 RIDGE_ROWS = 312.5               # rows per expert where weight streaming stops bounding (bf16 and fp8)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 EXPERTS_SRC = os.path.join(ROOT, "expert_routed_ffn_amd", "csrc", "experts.hip")
-DEFAULT_CONFIGS = "skew_t64,prefill_t2048,prefill_fp8_t16384,prefill_bf16_t16384"
+DEFAULT_CONFIGS = ("skew_t64,prefill_t2048,prefill_fp8_t16384,prefill_bf16_t16384,"
+                   "decode_t8_mxfp4,skew_t64_mxfp4")
 METRIC = "MoE-layer tokens/s (one Beam MoE layer forward incl. routing and norm boundary)"
 
 
@@ -118,12 +120,13 @@ def layer_setup(wl, stacks, dev):
     w_r, bias = synth.make_router(wl, dev)
     x, h, gp, gq = synth.make_activations(wl, dev)
     fp8 = wl.w_dtype == "fp8"
-    w_dt = beam.BEAM_FP8_E4M3 if fp8 else beam.BEAM_BF16
+    mx = wl.w_dtype == "mxfp4"
+    w_dt = beam.BEAM_FP8_E4M3 if fp8 else (beam.BEAM_MXFP4 if mx else beam.BEAM_BF16)
     bufs = beam.alloc_buffers(lcfg(wl), wl.T, x.dtype, w_dt, y_dtype=torch.bfloat16 if fp8 else torch.float32,
                               device=dev)
     wgu, wd, sgu, sd = stacks
     return dict(cfg=lcfg(wl), w_r=w_r, bias=bias, x=x, h=h.clone(), h0=h, gp=gp, gq=gq, bufs=bufs,
-                wgu=wgu, wd=wd, sgu=sgu, sd=sd, fp8=fp8)
+                wgu=wgu, wd=wd, sgu=sgu, sd=sd, fp8=fp8, mx=mx)
 
 
 def run_step(wl, s, hipev=None, evs=None, stream=None):
@@ -135,11 +138,14 @@ def run_step(wl, s, hipev=None, evs=None, stream=None):
     mark = (lambda i: hipev.record(evs[i], stream)) if evs is not None else (lambda i: None)
     mark(0)
     beam.beam_moe_route(cfg, s["x"], s["w_r"], s["bias"], b.topk_ids, b.topk_w, b.logits, b.ws)
+    if s["mx"]:   # run-time input quantisation of the 4-bit experts (timed in the route stage)
+        beam.beam_moe_quantize_mx(cfg, s["x"], b.x_q, b.x_scale)
     mark(1)
     beam.beam_moe_permute(cfg, b.topk_ids, b.expert_offsets, b.row_token, b.pair_row,
-                          x=s["x"] if s["fp8"] else None, x_q=b.x_q, x_scale=b.x_scale, ws=b.ws)
+                          x=s["x"] if s["fp8"] else None, x_q=b.x_q if s["fp8"] else None,
+                          x_scale=b.x_scale if s["fp8"] else None, ws=b.ws)
     mark(2)
-    beam.beam_moe_experts(cfg, wl.T, b.x_q if s["fp8"] else s["x"], b.expert_offsets, b.row_token,
+    beam.beam_moe_experts(cfg, wl.T, b.x_q if (s["fp8"] or s["mx"]) else s["x"], b.expert_offsets, b.row_token,
                           s["wgu"], s["wd"], b.y, x_scale=b.x_scale, s_gate_up=s["sgu"], s_down=s["sd"],
                           ws=b.ws)
     mark(3)
@@ -206,9 +212,14 @@ def algorithmic(wl, D):
     Flops per (token, expert) pair: 2*H*2F (GEMM1) + 2*F*H (GEMM2)."""
     H, F, T, K, E = wl.hidden, wl.d_ff, wl.T, wl.topk, wl.n_experts
     fp8 = wl.w_dtype == "fp8"
-    es = 1 if fp8 else 2
-    w_expert = 3 * H * F * es + ((2 * F + H) * 4 if fp8 else 0)
-    x_read = T * H * (1 if fp8 else 2) + (T * 4 if fp8 else 0)     # the GEMM input: e4m3 codes + scales, or bf16
+    mx = wl.w_dtype == "mxfp4"
+    if mx:    # E2M1 half-bytes plus one E8M0 byte per 32 weights / activations
+        w_expert = 3 * H * F // 2 + 3 * H * F // 32
+        x_read = T * H // 2 + T * H // 32
+    else:
+        es = 1 if fp8 else 2
+        w_expert = 3 * H * F * es + ((2 * F + H) * 4 if fp8 else 0)
+        x_read = T * H * (1 if fp8 else 2) + (T * 4 if fp8 else 0)     # the GEMM input: e4m3 codes + scales, or bf16
     experts_bytes = D * w_expert + x_read
     layer_bytes = D * w_expert + E * H * 4 + 4 * T * H * 2
     experts_flops = 6 * H * F * T * K
@@ -235,6 +246,7 @@ def roofline_entry(wl, r):
     D = r["touched"]
     alg = algorithmic(wl, D)
     fp8 = wl.w_dtype == "fp8"
+    mx = wl.w_dtype == "mxfp4"
     ex_us = sum(r["per"]["experts"]) / len(r["per"]["experts"])
     ex_s = ex_us / 1e6
     rows_per_expert = wl.T * wl.topk / max(D, 1)
@@ -249,7 +261,8 @@ def roofline_entry(wl, r):
                 "frac": round(ach / HBM_PEAK_GBS, 4), "algorithmic_bytes": alg["experts_bytes"]}
     roof.update({"traffic": traffic_for(wl.name),
                  "kernel": "beam_moe_experts call (work items, GEMM1 + SwiGLU, GEMM2"
-                           + (", e4m3 re-quantisation of a" if fp8 else "") + ")",
+                           + (", e4m3 re-quantisation of a" if fp8 else "")
+                           + (", MXFP4 quantisation of a" if mx else "") + ")",
                  "kernel_avg_us": round(ex_us, 2)})
     step_s = r["ms_per_step"] / 1e3
     peak_f = FP8_MFMA_TFLOPS if fp8 else BF16_MFMA_TFLOPS

@@ -24,13 +24,13 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libbeam_moe.so")
 
-BEAM_F32, BEAM_BF16, BEAM_FP8_E4M3 = 0, 1, 2
+BEAM_F32, BEAM_BF16, BEAM_FP8_E4M3, BEAM_MXFP4 = 0, 1, 2, 3
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape or dtype",
           3: "workspace missing or too small", 4: "HIP launch failed"}
 
-SYMBOLS = ("beam_moe_route", "beam_moe_permute", "beam_moe_experts", "beam_moe_experts_static",
-           "beam_moe_combine_norm", "beam_moe_pack_weights", "beam_moe_workspace_bytes",
-           "beam_moe_status_string")
+SYMBOLS = ("beam_moe_route", "beam_moe_permute", "beam_moe_quantize_mx", "beam_moe_experts",
+           "beam_moe_experts_static", "beam_moe_combine_norm", "beam_moe_pack_weights",
+           "beam_moe_workspace_bytes", "beam_moe_status_string")
 STATIC_SCRATCH_BYTES = 64 << 20   # BEAM_MOE_STATIC_SCRATCH_BYTES
 
 
@@ -85,14 +85,15 @@ def lib() -> ctypes.CDLL:
     L.beam_moe_experts.argtypes = [cfgp, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32,
                                    vp, sz, vp]
     L.beam_moe_experts_static.argtypes = [cfgp, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp]
+    L.beam_moe_quantize_mx.argtypes = [cfgp, i32, vp, i32, vp, vp, vp]
     L.beam_moe_combine_norm.argtypes = [cfgp, i32, vp, i32, vp, vp, vp, vp, i32, vp, vp, i32, vp, vp]
     L.beam_moe_pack_weights.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp]
     L.beam_moe_workspace_bytes.argtypes = [cfgp, i32, i32]
     L.beam_moe_workspace_bytes.restype = sz
     L.beam_moe_status_string.argtypes = [i32]
     L.beam_moe_status_string.restype = ctypes.c_char_p
-    for f in ("beam_moe_route", "beam_moe_permute", "beam_moe_experts", "beam_moe_experts_static",
-              "beam_moe_combine_norm", "beam_moe_pack_weights"):
+    for f in ("beam_moe_route", "beam_moe_permute", "beam_moe_quantize_mx", "beam_moe_experts",
+              "beam_moe_experts_static", "beam_moe_combine_norm", "beam_moe_pack_weights"):
         getattr(L, f).restype = i32
     _lib = L
     return L
@@ -187,21 +188,32 @@ def beam_moe_permute(cfg: LayerCfg, topk_ids, expert_offsets, row_token, pair_ro
     _ok("beam_moe_permute", st)
 
 
+def beam_moe_quantize_mx(cfg: LayerCfg, x, x_q, x_scale, stream=None):
+    """Run-time MXFP4 quantisation of x [T,H] (bf16/f32) into packed E2M1
+    codes x_q [T,H/2] and E8M0 block scales x_scale [T,H/32] (uint8)."""
+    T, H = x.shape[0], cfg.hidden
+    _check(x, (T, H), (torch.bfloat16, torch.float32), "x")
+    _check(x_q, (T, H // 2), (torch.uint8,), "x_q")
+    _check(x_scale, (T, H // 32), (torch.uint8,), "x_scale")
+    st = lib().beam_moe_quantize_mx(ctypes.byref(cfg.c()), T, _p(x), _dt(x), _p(x_q), _p(x_scale),
+                                    _stream(stream))
+    _ok("beam_moe_quantize_mx", st)
+
+
+def _w_dtype(w_gate_up, s_gate_up):
+    """MXFP4 stacks are uint8 E2M1 bytes with uint8 E8M0 scales; fp8 stacks
+    carry fp32 row scales."""
+    if w_gate_up.dtype == torch.uint8 and s_gate_up is not None and s_gate_up.dtype == torch.uint8:
+        return BEAM_MXFP4
+    return _dt(w_gate_up)
+
+
 def beam_moe_experts(cfg: LayerCfg, T, x, expert_offsets, row_token, w_gate_up, w_down, y,
                      x_scale=None, s_gate_up=None, s_down=None, ws=None, stream=None):
-    """x: [T,H] f32/bf16 activations, or e4m3 codes (uint8) for fp8 weights."""
-    E, H, F, TK = cfg.n_experts, cfg.hidden, cfg.d_ff, T * cfg.topk
-    w_dt = _dt(w_gate_up)
-    _check(x, (T, H), (w_gate_up.dtype,) if w_dt != BEAM_FP8_E4M3 else (torch.uint8, torch.float8_e4m3fn), "x")
-    _check(expert_offsets, (E + 1,), (torch.int32,), "expert_offsets")
-    _check(row_token, (TK,), (torch.int32,), "row_token")
-    _check(w_gate_up, (E, 2 * F, H), (w_gate_up.dtype,), "w_gate_up")
-    _check(w_down, (E, H, F), (w_gate_up.dtype,), "w_down")
-    _check(y, (TK, H), (torch.float32, torch.bfloat16), "y")
-    if w_dt == BEAM_FP8_E4M3:
-        _check(x_scale, (T,), (torch.float32,), "x_scale")
-        _check(s_gate_up, (E, 2 * F), (torch.float32,), "s_gate_up")
-        _check(s_down, (E, H), (torch.float32,), "s_down")
+    """x: [T,H] f32/bf16 activations, e4m3 codes (uint8) for fp8 weights, or
+    packed E2M1 codes [T,H/2] for MXFP4 weights."""
+    w_dt = _experts_common(cfg, T, x, expert_offsets, row_token, w_gate_up, w_down, y, x_scale,
+                           s_gate_up, s_down)
     st = lib().beam_moe_experts(ctypes.byref(cfg.c()), T, w_dt, _p(x), w_dt, _p(x_scale),
                                 _p(expert_offsets), _p(row_token), _p(w_gate_up), _p(s_gate_up),
                                 _p(w_down), _p(s_down), _p(y), _dt(y), _p(ws),
@@ -211,13 +223,21 @@ def beam_moe_experts(cfg: LayerCfg, T, x, expert_offsets, row_token, w_gate_up, 
 
 def _experts_common(cfg, T, x, expert_offsets, row_token, w_gate_up, w_down, y, x_scale, s_gate_up, s_down):
     E, H, F, TK = cfg.n_experts, cfg.hidden, cfg.d_ff, T * cfg.topk
-    w_dt = _dt(w_gate_up)
-    _check(x, (T, H), (w_gate_up.dtype,) if w_dt != BEAM_FP8_E4M3 else (torch.uint8, torch.float8_e4m3fn), "x")
+    w_dt = _w_dtype(w_gate_up, s_gate_up)
     _check(expert_offsets, (E + 1,), (torch.int32,), "expert_offsets")
     _check(row_token, (TK,), (torch.int32,), "row_token")
+    _check(y, (TK, H), (torch.float32, torch.bfloat16), "y")
+    if w_dt == BEAM_MXFP4:
+        _check(x, (T, H // 2), (torch.uint8,), "x")
+        _check(w_gate_up, (E, 2 * F, H // 2), (torch.uint8,), "w_gate_up")
+        _check(w_down, (E, H, F // 2), (torch.uint8,), "w_down")
+        _check(x_scale, (T, H // 32), (torch.uint8,), "x_scale")
+        _check(s_gate_up, (E, 2 * F, H // 32), (torch.uint8,), "s_gate_up")
+        _check(s_down, (E, H, F // 32), (torch.uint8,), "s_down")
+        return w_dt
+    _check(x, (T, H), (w_gate_up.dtype,) if w_dt != BEAM_FP8_E4M3 else (torch.uint8, torch.float8_e4m3fn), "x")
     _check(w_gate_up, (E, 2 * F, H), (w_gate_up.dtype,), "w_gate_up")
     _check(w_down, (E, H, F), (w_gate_up.dtype,), "w_down")
-    _check(y, (TK, H), (torch.float32, torch.bfloat16), "y")
     if w_dt == BEAM_FP8_E4M3:
         _check(x_scale, (T,), (torch.float32,), "x_scale")
         _check(s_gate_up, (E, 2 * F), (torch.float32,), "s_gate_up")
@@ -257,37 +277,43 @@ def beam_moe_combine_norm(cfg: LayerCfg, y, pair_row, topk_w, h, x_next, gamma_p
     _ok("beam_moe_combine_norm", st)
 
 
-def beam_moe_pack_weights(cfg: LayerCfg, w_gate_up, w_down, packed_gate_up, packed_down, stream=None):
+def beam_moe_pack_weights(cfg: LayerCfg, w_gate_up, w_down, packed_gate_up, packed_down, stream=None,
+                          mxfp4=False):
     """Re-lays out [n,2F,H] / [n,H,F] expert stacks into the tiled layout that
-    beam_moe_experts reads (any n >= 1 experts)."""
+    beam_moe_experts reads (any n >= 1 experts).  mxfp4: the stacks are
+    packed E2M1 bytes [n,2F,H/2] / [n,H,F/2]."""
     n = w_gate_up.shape[0]
     H, F = cfg.hidden, cfg.d_ff
     dt = w_gate_up.dtype
-    _check(w_gate_up, (n, 2 * F, H), (dt,), "w_gate_up")
-    _check(w_down, (n, H, F), (dt,), "w_down")
-    _check(packed_gate_up, (n, 2 * F, H), (dt,), "packed_gate_up")
-    _check(packed_down, (n, H, F), (dt,), "packed_down")
-    st = lib().beam_moe_pack_weights(ctypes.byref(cfg.c()), n, _dt(w_gate_up), _p(w_gate_up), _p(w_down),
-                                     _p(packed_gate_up), _p(packed_down), _stream(stream))
+    d = 2 if mxfp4 else 1
+    _check(w_gate_up, (n, 2 * F, H // d), (dt,), "w_gate_up")
+    _check(w_down, (n, H, F // d), (dt,), "w_down")
+    _check(packed_gate_up, (n, 2 * F, H // d), (dt,), "packed_gate_up")
+    _check(packed_down, (n, H, F // d), (dt,), "packed_down")
+    st = lib().beam_moe_pack_weights(ctypes.byref(cfg.c()), n, BEAM_MXFP4 if mxfp4 else _dt(w_gate_up),
+                                     _p(w_gate_up), _p(w_down), _p(packed_gate_up), _p(packed_down),
+                                     _stream(stream))
     _ok("beam_moe_pack_weights", st)
 
 
 def packed_expert_stacks(cfg: LayerCfg, make_expert, n_experts: int, device="cuda"):
     """Builds packed [E,2F,H] / [E,H,F] stacks one expert at a time from
     make_expert(e) -> (w_gate_up [2F,H], w_down [H,F], s_gate_up, s_down)
-    device tensors.  Returns (packed_gate_up, packed_down, s_gate_up, s_down)."""
-    H, F = cfg.hidden, cfg.d_ff
+    device tensors (MXFP4: E2M1 bytes [2F,H/2] / [H,F/2] with uint8 E8M0
+    scales).  Returns (packed_gate_up, packed_down, s_gate_up, s_down); the
+    scales are not re-laid out."""
     a, b, c, d = make_expert(0)
-    pgu = torch.empty((n_experts, 2 * F, H), dtype=a.dtype, device=device)
-    pd = torch.empty((n_experts, H, F), dtype=b.dtype, device=device)
+    mx = c is not None and c.dtype == torch.uint8
+    pgu = torch.empty((n_experts,) + tuple(a.shape), dtype=a.dtype, device=device)
+    pd = torch.empty((n_experts,) + tuple(b.shape), dtype=b.dtype, device=device)
     sgu = sd = None
     if c is not None:
-        sgu = torch.empty((n_experts, 2 * F), dtype=torch.float32, device=device)
-        sd = torch.empty((n_experts, H), dtype=torch.float32, device=device)
+        sgu = torch.empty((n_experts,) + tuple(c.shape), dtype=c.dtype, device=device)
+        sd = torch.empty((n_experts,) + tuple(d.shape), dtype=d.dtype, device=device)
     for e in range(n_experts):
         if e:
             a, b, c, d = make_expert(e)
-        beam_moe_pack_weights(cfg, a.unsqueeze(0), b.unsqueeze(0), pgu[e:e + 1], pd[e:e + 1])
+        beam_moe_pack_weights(cfg, a.unsqueeze(0), b.unsqueeze(0), pgu[e:e + 1], pd[e:e + 1], mxfp4=mx)
         if sgu is not None:
             sgu[e].copy_(c)
             sd[e].copy_(d)
@@ -318,6 +344,13 @@ def alloc_buffers(cfg: LayerCfg, T: int, act_dtype, w_dtype: int, y_dtype=torch.
     TK = T * cfg.topk
     d = dict(device=device)
     fp8 = w_dtype == BEAM_FP8_E4M3
+    mx = w_dtype == BEAM_MXFP4
+    if mx:
+        x_q = torch.empty((T, cfg.hidden // 2), dtype=torch.uint8, **d)
+        x_scale = torch.empty((T, cfg.hidden // 32), dtype=torch.uint8, **d)
+    else:
+        x_q = torch.empty((T, cfg.hidden), dtype=torch.uint8, **d) if fp8 else None
+        x_scale = torch.empty((T,), dtype=torch.float32, **d) if fp8 else None
     return LayerBuffers(
         topk_ids=torch.empty((T, cfg.topk), dtype=torch.int32, **d),
         topk_w=torch.empty((T, cfg.topk), dtype=torch.float32, **d),
@@ -325,8 +358,8 @@ def alloc_buffers(cfg: LayerCfg, T: int, act_dtype, w_dtype: int, y_dtype=torch.
         expert_offsets=torch.empty((cfg.n_experts + 1,), dtype=torch.int32, **d),
         row_token=torch.empty((TK,), dtype=torch.int32, **d),
         pair_row=torch.empty((TK,), dtype=torch.int32, **d),
-        x_q=torch.empty((T, cfg.hidden), dtype=torch.uint8, **d) if fp8 else None,
-        x_scale=torch.empty((T,), dtype=torch.float32, **d) if fp8 else None,
+        x_q=x_q,
+        x_scale=x_scale,
         y=torch.empty((TK, cfg.hidden), dtype=y_dtype, **d),
         x_next=torch.empty((T, cfg.hidden), dtype=act_dtype, **d),
         moe_out=torch.empty((T, cfg.hidden), dtype=torch.float32, **d) if keep_moe_out else None,
@@ -340,12 +373,16 @@ def moe_layer(cfg: LayerCfg, x, w_router, bias, w_gate_up, w_down, h, gamma_post
     are packed stacks (beam_moe_pack_weights).  h is updated in place; the
     other results land in `bufs`."""
     T = x.shape[0]
-    fp8 = _dt(w_gate_up) == BEAM_FP8_E4M3
+    w_dt = _w_dtype(w_gate_up, s_gate_up)
+    fp8 = w_dt == BEAM_FP8_E4M3
+    mx = w_dt == BEAM_MXFP4
     beam_moe_route(cfg, x, w_router, bias, bufs.topk_ids, bufs.topk_w, bufs.logits, bufs.ws, stream)
+    if mx:
+        beam_moe_quantize_mx(cfg, x, bufs.x_q, bufs.x_scale, stream)
     beam_moe_permute(cfg, bufs.topk_ids, bufs.expert_offsets, bufs.row_token, bufs.pair_row,
-                     x=x if fp8 else None, x_q=bufs.x_q, x_scale=bufs.x_scale, ws=bufs.ws,
-                     stream=stream)
-    beam_moe_experts(cfg, T, bufs.x_q if fp8 else x, bufs.expert_offsets, bufs.row_token,
+                     x=x if fp8 else None, x_q=bufs.x_q if fp8 else None,
+                     x_scale=bufs.x_scale if fp8 else None, ws=bufs.ws, stream=stream)
+    beam_moe_experts(cfg, T, bufs.x_q if (fp8 or mx) else x, bufs.expert_offsets, bufs.row_token,
                      w_gate_up, w_down, bufs.y, x_scale=bufs.x_scale, s_gate_up=s_gate_up,
                      s_down=s_down, ws=bufs.ws, stream=stream)
     beam_moe_combine_norm(cfg, bufs.y, bufs.pair_row, bufs.topk_w, h, bufs.x_next, gamma_post,

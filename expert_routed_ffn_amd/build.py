@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libbeam_moe.so")
-SOURCES = ["beam_moe.hip", "route.hip", "permute.hip", "experts.hip", "combine_norm.hip", "pack.hip"]
+SOURCES = ["beam_moe.hip", "route.hip", "permute.hip", "experts.hip", "combine_norm.hip", "pack.hip", "mx.hip"]
 
 ARCH = "gfx950"
 HIP_FLAGS = [

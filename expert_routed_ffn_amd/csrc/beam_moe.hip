@@ -45,7 +45,9 @@ beam_status check_cfg(const beam_moe_cfg* c) {
     return BEAM_OK;
 }
 
-bool valid_dtype(beam_dtype d) { return d == BEAM_F32 || d == BEAM_BF16 || d == BEAM_FP8_E4M3; }
+bool valid_dtype(beam_dtype d) {
+    return d == BEAM_F32 || d == BEAM_BF16 || d == BEAM_FP8_E4M3 || d == BEAM_MXFP4;
+}
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -54,15 +56,23 @@ size_t route_ws(const beam_moe_cfg* c, int T) {
 }
 
 beam::WKind wkind(beam_dtype d) {
-    return d == BEAM_BF16 ? beam::W_BF16 : (d == BEAM_FP8_E4M3 ? beam::W_FP8 : beam::W_F32);
+    switch (d) {
+        case BEAM_BF16: return beam::W_BF16;
+        case BEAM_FP8_E4M3: return beam::W_FP8;
+        case BEAM_MXFP4: return beam::W_MXFP4;
+        default: return beam::W_F32;
+    }
 }
+
+// 4-bit experts: rows of K values are K/2 bytes in whole 256-byte chunks
+bool mx_shape_ok(const beam_moe_cfg* c) { return c->hidden % 512 == 0 && c->d_ff % 512 == 0; }
 
 // Checks of beam_moe_experts that do not concern the workspace; fills `a`
 // (all but a.ws) and the workspace bytes the call needs.
 beam_status experts_prepare(const beam_moe_cfg* cfg, int32_t T, beam_dtype w_dtype, const void* x,
-                            beam_dtype x_dtype, const float* x_scale, const int32_t* expert_offsets,
-                            const int32_t* row_token, const void* w_gate_up, const float* s_gate_up,
-                            const void* w_down, const float* s_down, void* y, beam_dtype y_dtype,
+                            beam_dtype x_dtype, const void* x_scale, const int32_t* expert_offsets,
+                            const int32_t* row_token, const void* w_gate_up, const void* s_gate_up,
+                            const void* w_down, const void* s_down, void* y, beam_dtype y_dtype,
                             beam::ExpertsArgs& a, size_t& need) {
     beam_status st = check_cfg(cfg);
     if (st != BEAM_OK) return st;
@@ -70,12 +80,15 @@ beam_status experts_prepare(const beam_moe_cfg* cfg, int32_t T, beam_dtype w_dty
     if (!valid_dtype(w_dtype) || !valid_dtype(x_dtype) || !valid_dtype(y_dtype))
         return BEAM_ERR_INVALID_ARG;
     if (x_dtype != w_dtype) return BEAM_ERR_INVALID_ARG;
-    if (y_dtype == BEAM_FP8_E4M3) return BEAM_ERR_INVALID_ARG;
+    if (y_dtype == BEAM_FP8_E4M3 || y_dtype == BEAM_MXFP4) return BEAM_ERR_INVALID_ARG;
     if (w_dtype == BEAM_FP8_E4M3 && (cfg->hidden % 256 != 0 || cfg->d_ff % 256 != 0))
+        return BEAM_ERR_UNSUPPORTED;
+    if (w_dtype == BEAM_MXFP4 && (!mx_shape_ok(cfg) || (int64_t)T * cfg->topk >= 256LL * cfg->n_experts))
         return BEAM_ERR_UNSUPPORTED;
     if (T == 0) return BEAM_OK;
     if (!x || !expert_offsets || !row_token || !w_gate_up || !w_down || !y) return BEAM_ERR_INVALID_ARG;
-    if (w_dtype == BEAM_FP8_E4M3 && (!x_scale || !s_gate_up || !s_down)) return BEAM_ERR_INVALID_ARG;
+    if ((w_dtype == BEAM_FP8_E4M3 || w_dtype == BEAM_MXFP4) && (!x_scale || !s_gate_up || !s_down))
+        return BEAM_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(y))
         return BEAM_ERR_INVALID_ARG;
     if (w_dtype == BEAM_FP8_E4M3 && (!aligned16(s_gate_up) || !aligned16(s_down)))
@@ -230,9 +243,9 @@ beam_status beam_moe_permute(const beam_moe_cfg* cfg, int32_t T, const int32_t* 
 }
 
 beam_status beam_moe_experts(const beam_moe_cfg* cfg, int32_t T, beam_dtype w_dtype, const void* x,
-                             beam_dtype x_dtype, const float* x_scale, const int32_t* expert_offsets,
-                             const int32_t* row_token, const void* w_gate_up, const float* s_gate_up,
-                             const void* w_down, const float* s_down, void* y, beam_dtype y_dtype,
+                             beam_dtype x_dtype, const void* x_scale, const int32_t* expert_offsets,
+                             const int32_t* row_token, const void* w_gate_up, const void* s_gate_up,
+                             const void* w_down, const void* s_down, void* y, beam_dtype y_dtype,
                              void* ws, size_t ws_bytes, void* stream) {
     beam::ExpertsArgs a{};
     size_t need = 0;
@@ -246,10 +259,10 @@ beam_status beam_moe_experts(const beam_moe_cfg* cfg, int32_t T, beam_dtype w_dt
 }
 
 beam_status beam_moe_experts_static(const beam_moe_cfg* cfg, int32_t T, beam_dtype w_dtype,
-                                    const void* x, beam_dtype x_dtype, const float* x_scale,
+                                    const void* x, beam_dtype x_dtype, const void* x_scale,
                                     const int32_t* expert_offsets, const int32_t* row_token,
-                                    const void* w_gate_up, const float* s_gate_up, const void* w_down,
-                                    const float* s_down, void* y, beam_dtype y_dtype, void* stream) {
+                                    const void* w_gate_up, const void* s_gate_up, const void* w_down,
+                                    const void* s_down, void* y, beam_dtype y_dtype, void* stream) {
     beam::ExpertsArgs a{};
     size_t need = 0;
     const beam_status st = experts_prepare(cfg, T, w_dtype, x, x_dtype, x_scale, expert_offsets, row_token,
@@ -273,13 +286,15 @@ beam_status beam_moe_pack_weights(const beam_moe_cfg* cfg, int32_t n_experts, be
     if (n_experts < 0 || !valid_dtype(w_dtype)) return BEAM_ERR_INVALID_ARG;
     if (w_dtype == BEAM_FP8_E4M3 && (cfg->hidden % 256 != 0 || cfg->d_ff % 256 != 0))
         return BEAM_ERR_UNSUPPORTED;
+    if (w_dtype == BEAM_MXFP4 && !mx_shape_ok(cfg)) return BEAM_ERR_UNSUPPORTED;
     if (n_experts == 0) return BEAM_OK;
     if (!w_gate_up || !w_down || !packed_gate_up || !packed_down) return BEAM_ERR_INVALID_ARG;
     if (!aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(packed_gate_up) || !aligned16(packed_down))
         return BEAM_ERR_INVALID_ARG;
-    const size_t es = w_dtype == BEAM_F32 ? 4 : (w_dtype == BEAM_BF16 ? 2 : 1);
+    // bytes per 2 elements
+    const size_t es2 = w_dtype == BEAM_F32 ? 8 : (w_dtype == BEAM_BF16 ? 4 : (w_dtype == BEAM_FP8_E4M3 ? 2 : 1));
     const size_t H = cfg->hidden, F = cfg->d_ff, E = (size_t)n_experts;
-    const size_t gu_bytes = E * 2 * F * H * es, d_bytes = E * H * F * es;
+    const size_t gu_bytes = E * 2 * F * H * es2 / 2, d_bytes = E * H * F * es2 / 2;
     auto overlap = [](const void* a, size_t na, const void* b, size_t nb) {
         const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
         return x < y + nb && y < x + na;
@@ -294,10 +309,26 @@ beam_status beam_moe_pack_weights(const beam_moe_cfg* cfg, int32_t n_experts, be
         if (err == hipSuccess)
             err = hipMemcpyAsync(packed_down, w_down, d_bytes, hipMemcpyDeviceToDevice, s);
     } else {
-        err = beam::launch_pack(w_gate_up, packed_gate_up, E * 2 * F, (int)(H * es), s);
-        if (err == hipSuccess) err = beam::launch_pack(w_down, packed_down, E * H, (int)(F * es), s);
+        err = beam::launch_pack(w_gate_up, packed_gate_up, E * 2 * F, (int)(H * es2 / 2), s);
+        if (err == hipSuccess) err = beam::launch_pack(w_down, packed_down, E * H, (int)(F * es2 / 2), s);
     }
     return err == hipSuccess ? BEAM_OK : BEAM_ERR_HIP;
+}
+
+beam_status beam_moe_quantize_mx(const beam_moe_cfg* cfg, int32_t T, const void* x, beam_dtype x_dtype,
+                                 uint8_t* x_q, uint8_t* x_scale, void* stream) {
+    beam_status st = check_cfg(cfg);
+    if (st != BEAM_OK) return st;
+    if (T < 0 || T > kMaxT) return BEAM_ERR_INVALID_ARG;
+    if (x_dtype != BEAM_BF16 && x_dtype != BEAM_F32) return BEAM_ERR_INVALID_ARG;
+    if (cfg->hidden % 512 != 0) return BEAM_ERR_UNSUPPORTED;
+    if (T == 0) return BEAM_OK;
+    if (!x || !x_q || !x_scale) return BEAM_ERR_INVALID_ARG;
+    if (!aligned16(x) || (reinterpret_cast<uintptr_t>(x_q) & 3u) != 0) return BEAM_ERR_INVALID_ARG;
+    return beam::launch_quantize_mx(x, x_dtype == BEAM_BF16, T, cfg->hidden, nullptr, x_q, x_scale,
+                                    static_cast<hipStream_t>(stream)) == hipSuccess
+               ? BEAM_OK
+               : BEAM_ERR_HIP;
 }
 
 beam_status beam_moe_combine_norm(const beam_moe_cfg* cfg, int32_t T, const void* y,

@@ -62,6 +62,33 @@ __global__ __launch_bounds__(256) void beam_build_items(const int32_t* __restric
 
 typedef int i32x4v __attribute__((ext_vector_type(4)));
 
+// bytes of one row of k values
+template <int KIND> BEAM_DEV constexpr int row_bytes(int k) {
+    return KIND == W_BF16 ? 2 * k : (KIND == W_MXFP4 ? k / 2 : k);
+}
+
+// One 256-byte K iteration of MXFP4 operands (512 E2M1 values of the row):
+// piece s is one K = 128 MFMA in which lane (r, g) holds the 32 values of
+// block 4 s + g of the iteration, i.e. bytes [64 s + 16 g, +16) -- the same
+// bytes on the weight (A) and the activation (B) side.  sa / sb hold the
+// 16 E8M0 codes of the iteration's blocks for the lane's weight row /
+// activation row; block 4 s + g is byte g of word s.
+BEAM_DEV void mfma_kiter_mx(const uint4 (&a)[4], const uint4 (&b)[4], const uint4& sa, const uint4& sb,
+                            f32x4& acc) {
+    const int sh = 8 * ((threadIdx.x & 63) >> 4);
+    const uint32_t wa[4] = {sa.x, sa.y, sa.z, sa.w};
+    const uint32_t wb[4] = {sb.x, sb.y, sb.z, sb.w};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const i32x8 av = {(int)a[s].x, (int)a[s].y, (int)a[s].z, (int)a[s].w, 0, 0, 0, 0};
+        const i32x8 bv = {(int)b[s].x, (int)b[s].y, (int)b[s].z, (int)b[s].w, 0, 0, 0, 0};
+        // formats 4/4 = E2M1 x E2M1 (the low 4 dwords of each operand);
+        // per-lane E8M0 scales from byte 0 of the shifted words
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 4, 4, 0, (int)((wa[s] >> sh) & 0xFF),
+                                                               0, (int)((wb[s] >> sh) & 0xFF));
+    }
+}
+
 template <int KIND>
 BEAM_DEV void mfma_kiter(const uint4 (&a)[4], const uint4 (&b)[4], f32x4& acc) {
     if constexpr (KIND == W_BF16) {
@@ -93,6 +120,8 @@ struct GemmParams {
     const float* act_scale;    // fp8: G1 per token, G2 per row
     const uint8_t* W;          // expert weight stacks
     const float* wscale;       // fp8: per output row
+    const uint8_t* mx_act;     // MXFP4: E8M0 codes of the activation rows [rows, K/32]
+    const uint8_t* mx_w;       // MXFP4: E8M0 codes of the weight rows [E, rows, K/32]
     int H, F;
     void* out;
     bool out_bf16;             // G2 only
@@ -120,6 +149,10 @@ BEAM_DEV void store_swiglu(const GemmParams& p, int e, int f, size_t row, int to
         av.y = silu_f32(gv[1]) * uv[1];
         av.z = silu_f32(gv[2]) * uv[2];
         av.w = silu_f32(gv[3]) * uv[3];
+        *reinterpret_cast<float4*>(static_cast<float*>(p.out) + row * p.F + f) = av;
+    } else if constexpr (KIND == W_MXFP4) {   // the MX scales are inside the MFMA
+        const float4 av = make_float4(silu_f32(gv[0]) * uv[0], silu_f32(gv[1]) * uv[1],
+                                      silu_f32(gv[2]) * uv[2], silu_f32(gv[3]) * uv[3]);
         *reinterpret_cast<float4*>(static_cast<float*>(p.out) + row * p.F + f) = av;
     } else {
         uint16_t hb[4];
@@ -174,9 +207,8 @@ BEAM_DEV void store_block(const GemmParams& p, int e, int a0, int a1, size_t row
 template <int KIND, bool G1>
 BEAM_DEV void weight_rows(const GemmParams& p, int e, int tile, int& a0, int& a1, const uint8_t*& pa0,
                           const uint8_t*& pa1) {
-    constexpr int ES = (KIND == W_BF16) ? 2 : 1;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int kbytes = (G1 ? p.H : p.F) * ES;
+    const int kbytes = row_bytes<KIND>(G1 ? p.H : p.F);
     const int nrows_w = G1 ? 2 * p.F : p.H;
     a0 = G1 ? tile * 64 + wave * 16 : tile * 128 + wave * 32;
     a1 = G1 ? p.F + a0 : a0 + 16;
@@ -189,10 +221,9 @@ BEAM_DEV void weight_rows(const GemmParams& p, int e, int tile, int& a0, int& a1
 // ---- small items (<= 16 rows): B fragments straight from L2 into registers
 template <int KIND, bool G1>
 BEAM_DEV void gemm_item_direct(const GemmParams& p, int e, int row0, int rows, int tile) {
-    constexpr int ES = (KIND == W_BF16) ? 2 : 1;
     const int lane = threadIdx.x & 63;
     const int r = lane & 15, g = lane >> 4;
-    const int kbytes = (G1 ? p.H : p.F) * ES;
+    const int kbytes = row_bytes<KIND>(G1 ? p.H : p.F);
     int a0, a1;
     const uint8_t *pa0, *pa1;
     weight_rows<KIND, G1>(p, e, tile, a0, a1, pa0, pa1);
@@ -208,8 +239,20 @@ BEAM_DEV void gemm_item_direct(const GemmParams& p, int e, int row0, int rows, i
         pb = p.act + (size_t)(bval ? row0 + r : row0) * kbytes + 16 * g;
     }
 
+    // MXFP4: E8M0 rows of the lane's two weight rows and its activation row;
+    // a 256-byte K iteration covers 16 blocks = 16 scale bytes
+    const uint8_t *psa0 = nullptr, *psa1 = nullptr, *psb = nullptr;
+    if constexpr (KIND == W_MXFP4) {
+        const int kblk = (G1 ? p.H : p.F) / 32;
+        const size_t wrow0 = (size_t)e * (G1 ? 2 * p.F : p.H);
+        psa0 = p.mx_w + (wrow0 + a0 + r) * kblk;
+        psa1 = p.mx_w + (wrow0 + a1 + r) * kblk;
+        psb = p.mx_act + (size_t)(G1 ? tok : (bval ? row0 + r : row0)) * kblk;
+    }
+
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     uint4 wa0[2][4], wa1[2][4], xb[2][4];
+    uint4 sa0[2], sa1[2], sb[2];
     auto load = [&](int buf, int k) {
         // k: byte offset along the row, a multiple of 256 (one packed tile)
 #pragma unroll
@@ -219,10 +262,20 @@ BEAM_DEV void gemm_item_direct(const GemmParams& p, int e, int row0, int rows, i
         }
 #pragma unroll
         for (int s = 0; s < 4; ++s) xb[buf][s] = bval ? ld16(pb + k + 64 * s) : make_uint4(0, 0, 0, 0);
+        if constexpr (KIND == W_MXFP4) {
+            sa0[buf] = ld16(psa0 + k / 16);
+            sa1[buf] = ld16(psa1 + k / 16);
+            sb[buf] = ld16(psb + k / 16);
+        }
     };
     auto compute = [&](int buf) {
-        mfma_kiter<KIND>(wa0[buf], xb[buf], acc0);
-        mfma_kiter<KIND>(wa1[buf], xb[buf], acc1);
+        if constexpr (KIND == W_MXFP4) {
+            mfma_kiter_mx(wa0[buf], xb[buf], sa0[buf], sb[buf], acc0);
+            mfma_kiter_mx(wa1[buf], xb[buf], sa1[buf], sb[buf], acc1);
+        } else {
+            mfma_kiter<KIND>(wa0[buf], xb[buf], acc0);
+            mfma_kiter<KIND>(wa1[buf], xb[buf], acc1);
+        }
     };
 
     load(0, 0);
@@ -248,11 +301,10 @@ BEAM_DEV int lds_pos(int rr, int c) { return rr * 16 + (c ^ (rr & 15)); }
 
 template <int KIND, bool G1, int NB, bool NT>
 BEAM_DEV void gemm_item_lds(const GemmParams& p, int e, int row0, int rows, int tile,
-                            uint4 (*bs)[kLdsRows * 16]) {
-    constexpr int ES = (KIND == W_BF16) ? 2 : 1;
+                            uint4 (*bs)[kLdsRows * 16], uint4 (*bss)[kLdsRows]) {
     const int lane = threadIdx.x & 63;
     const int r = lane & 15, g = lane >> 4;
-    const int kbytes = (G1 ? p.H : p.F) * ES;
+    const int kbytes = row_bytes<KIND>(G1 ? p.H : p.F);
     const int nk = kbytes / kKIterBytes;
     int a0, a1;
     const uint8_t *pa0, *pa1;
@@ -272,13 +324,39 @@ BEAM_DEV void gemm_item_lds(const GemmParams& p, int e, int row0, int rows, int 
         src[i] = p.act + srow * kbytes + 16 * lc;
     }
     uint4 stage[NB];
+    // MXFP4: the staged rows' E8M0 codes (16 per 256-byte K iteration) go to
+    // LDS too, copied by the chunk-0 thread of each row; the lane's weight
+    // rows' codes stream into registers with the weights
+    const uint8_t* ssrc[NB];
+    uint4 sstage[NB];
+    const uint8_t *psa0 = nullptr, *psa1 = nullptr;
+    uint4 sa0[2], sa1[2];
+    if constexpr (KIND == W_MXFP4) {
+        const int kblk = (G1 ? p.H : p.F) / 32;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) ssrc[i] = p.mx_act + (size_t)((src[i] - p.act) / kbytes) * kblk;
+        const size_t wrow0 = (size_t)e * (G1 ? 2 * p.F : p.H);
+        psa0 = p.mx_w + (wrow0 + a0 + r) * kblk;
+        psa1 = p.mx_w + (wrow0 + a1 + r) * kblk;
+    }
     auto gload = [&](int k) {
 #pragma unroll
         for (int i = 0; i < NB; ++i) stage[i] = sval[i] ? ld16(src[i] + k) : make_uint4(0, 0, 0, 0);
+        if constexpr (KIND == W_MXFP4) {
+#pragma unroll
+            for (int i = 0; i < NB; ++i)
+                sstage[i] = (sval[i] && lc == 0) ? ld16(ssrc[i] + k / 16) : make_uint4(0, 0, 0, 0);
+        }
     };
     auto swrite = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < NB; ++i) bs[buf][lds_pos(lr + 16 * i, lc)] = stage[i];
+        if constexpr (KIND == W_MXFP4) {
+            if (lc == 0) {
+#pragma unroll
+                for (int i = 0; i < NB; ++i) bss[buf][lr + 16 * i] = sstage[i];
+            }
+        }
     };
 
     f32x4 acc0[NB], acc1[NB];
@@ -299,6 +377,10 @@ BEAM_DEV void gemm_item_lds(const GemmParams& p, int e, int row0, int rows, int 
                 wa1[buf][s] = ld16(pa1 + (size_t)k * 16 + 1024 * s);
             }
         }
+        if constexpr (KIND == W_MXFP4) {
+            sa0[buf] = ld16(psa0 + k / 16);
+            sa1[buf] = ld16(psa1 + k / 16);
+        }
     };
     // one K step on LDS buffer CUR; prefetches step kit+1 into the other buffer
     auto step = [&](auto curc, int kit) {
@@ -313,8 +395,14 @@ BEAM_DEV void gemm_item_lds(const GemmParams& p, int e, int row0, int rows, int 
             uint4 xb[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) xb[s] = bs[CUR][lds_pos(nb * 16 + r, 4 * s + g)];
-            mfma_kiter<KIND>(wa0[CUR], xb, acc0[nb]);
-            mfma_kiter<KIND>(wa1[CUR], xb, acc1[nb]);
+            if constexpr (KIND == W_MXFP4) {
+                const uint4 sb = bss[CUR][nb * 16 + r];
+                mfma_kiter_mx(wa0[CUR], xb, sa0[CUR], sb, acc0[nb]);
+                mfma_kiter_mx(wa1[CUR], xb, sa1[CUR], sb, acc1[nb]);
+            } else {
+                mfma_kiter<KIND>(wa0[CUR], xb, acc0[nb]);
+                mfma_kiter<KIND>(wa1[CUR], xb, acc1[nb]);
+            }
         }
         if (more) swrite(CUR ^ 1);
         __syncthreads();
@@ -349,15 +437,16 @@ __global__ __launch_bounds__(256) void beam_expert_gemm_direct(GemmParams p) {
 }
 
 template <int KIND, bool G1, bool NT>
-BEAM_DEV void dispatch_lds(const GemmParams& p, int4 it, int tile, uint4 (*bs)[kLdsRows * 16]) {
+BEAM_DEV void dispatch_lds(const GemmParams& p, int4 it, int tile, uint4 (*bs)[kLdsRows * 16],
+                           uint4 (*bss)[kLdsRows]) {
     if (it.z <= 16)
-        gemm_item_lds<KIND, G1, 1, NT>(p, it.x, it.y, it.z, tile, bs);
+        gemm_item_lds<KIND, G1, 1, NT>(p, it.x, it.y, it.z, tile, bs, bss);
     else if (it.z <= 32)
-        gemm_item_lds<KIND, G1, 2, NT>(p, it.x, it.y, it.z, tile, bs);
+        gemm_item_lds<KIND, G1, 2, NT>(p, it.x, it.y, it.z, tile, bs, bss);
     else if (it.z <= 64)
-        gemm_item_lds<KIND, G1, 4, NT>(p, it.x, it.y, it.z, tile, bs);
+        gemm_item_lds<KIND, G1, 4, NT>(p, it.x, it.y, it.z, tile, bs, bss);
     else
-        gemm_item_lds<KIND, G1, 8, NT>(p, it.x, it.y, it.z, tile, bs);
+        gemm_item_lds<KIND, G1, 8, NT>(p, it.x, it.y, it.z, tile, bs, bss);
 }
 
 // bf16: two waves per SIMD, so the 4-wave workgroups of two items overlap
@@ -366,14 +455,16 @@ BEAM_DEV void dispatch_lds(const GemmParams& p, int4 it, int tile, uint4 (*bs)[k
 template <int KIND, bool G1>
 __global__ __launch_bounds__(256, KIND == W_BF16 ? 2 : 1) void beam_expert_gemm_lds(GemmParams p) {
     __shared__ uint4 bs[2][kLdsRows * 16];
+    __shared__ uint4 bss[2][KIND == W_MXFP4 ? kLdsRows : 1];   // MXFP4 activation scales
     const int item = blockIdx.x / p.n_tiles;
     const int tile = blockIdx.x - item * p.n_tiles;
     if (item >= *p.n_items) return;
     const int4 it = p.items[item];
+    auto bssp = reinterpret_cast<uint4 (*)[kLdsRows]>(&bss[0][0]);
     // weights read once (single-item expert): non-temporal; shared by the
     // expert's other items: plain loads that stay in L2
-    if ((it.w & 0xFFFF) == 1) dispatch_lds<KIND, G1, true>(p, it, tile, bs);
-    else dispatch_lds<KIND, G1, false>(p, it, tile, bs);
+    if ((it.w & 0xFFFF) == 1) dispatch_lds<KIND, G1, true>(p, it, tile, bs, bssp);
+    else dispatch_lds<KIND, G1, false>(p, it, tile, bs, bssp);
 }
 
 // ---- wide tiles for large items: each wave owns FOUR 16-row weight tiles
@@ -383,9 +474,8 @@ __global__ __launch_bounds__(256, KIND == W_BF16 ? 2 : 1) void beam_expert_gemm_
 // 4 x NB accumulator tiles live in registers (AGPRs), one wave per SIMD.
 template <int KIND, bool G1>
 BEAM_DEV void wide_rows(const GemmParams& p, int e, int tile, int (&a)[4], const uint8_t* (&pa)[4]) {
-    constexpr int ES = (KIND == W_BF16) ? 2 : 1;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int kbytes = (G1 ? p.H : p.F) * ES;
+    const int kbytes = row_bytes<KIND>(G1 ? p.H : p.F);
     const int nrows_w = G1 ? 2 * p.F : p.H;
     if constexpr (G1) {
         const int f0 = tile * 128 + wave * 32;
@@ -409,11 +499,10 @@ BEAM_DEV i32x8 pair8(uint4 lo, uint4 hi) {
 template <int KIND, bool G1, int NB, bool NT>
 BEAM_DEV void gemm_item_wide(const GemmParams& p, int e, int row0, int rows, int tile,
                              uint4 (*bs)[kLdsRows * 16]) {
-    constexpr int ES = (KIND == W_BF16) ? 2 : 1;
     constexpr int NS = (KIND == W_BF16) ? 4 : 2;   // MFMA steps per 256-byte K iteration
     const int lane = threadIdx.x & 63;
     const int r = lane & 15, g = lane >> 4;
-    const int kbytes = (G1 ? p.H : p.F) * ES;
+    const int kbytes = row_bytes<KIND>(G1 ? p.H : p.F);
     const int nk = kbytes / kKIterBytes;
     int a[4];
     const uint8_t* pa[4];
@@ -639,9 +728,10 @@ static size_t max_items(int T, int K, int E) {
 struct ExpertsWs {
     int* n_items;
     int4* items;
-    void* a;        // bf16 [TK,F] (BF16) or fp32 [TK,F] (FP8, F32)
-    uint8_t* aq;    // FP8: e4m3 [TK,F]
+    void* a;        // bf16 [TK,F] (BF16) or fp32 [TK,F] (FP8, MXFP4, F32)
+    uint8_t* aq;    // FP8: e4m3 [TK,F]; MXFP4: packed E2M1 [TK,F/2]
     float* ascale;  // FP8: [TK]
+    uint8_t* amx;   // MXFP4: E8M0 [TK,F/32]
     size_t bytes;
 };
 
@@ -661,6 +751,12 @@ static ExpertsWs carve(void* base, int T, int K, int E, int F, WKind w) {
         off += align256(TK * F);
         s.ascale = reinterpret_cast<float*>(p + off);
         off += align256(TK * sizeof(float));
+    }
+    if (w == W_MXFP4) {
+        s.aq = p + off;
+        off += align256(TK * F / 2);
+        s.amx = p + off;
+        off += align256(TK * F / 32);
     }
     s.bytes = off;
     return s;
@@ -729,23 +825,39 @@ hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st) {
     // GEMM1 + SwiGLU
     p.act = static_cast<const uint8_t*>(a.x);
     p.row_token = a.row_token;
-    p.act_scale = a.xscale;
+    p.act_scale = static_cast<const float*>(a.xscale);
     p.W = static_cast<const uint8_t*>(a.wgu);
-    p.wscale = a.sgu;
+    p.wscale = static_cast<const float*>(a.sgu);
     p.out = ws.a;
     p.out_bf16 = false;
-    if (a.w == W_BF16)
+    if (a.w == W_MXFP4) {
+        p.act_scale = nullptr;
+        p.wscale = nullptr;
+        p.mx_act = static_cast<const uint8_t*>(a.xscale);
+        p.mx_w = static_cast<const uint8_t*>(a.sgu);
+        launch_gemm<W_MXFP4, true>(p, n_items_max, path, st);
+    } else if (a.w == W_BF16) {
         launch_gemm<W_BF16, true>(p, n_items_max, path, st);
-    else
+    } else {
         launch_gemm<W_FP8, true>(p, n_items_max, path, st);
+    }
 
     // GEMM2
     p.row_token = nullptr;
     p.W = static_cast<const uint8_t*>(a.wd);
-    p.wscale = a.sd;
+    p.wscale = static_cast<const float*>(a.sd);
     p.out = a.y;
     p.out_bf16 = a.y_bf16;
-    if (a.w == W_FP8) {
+    if (a.w == W_MXFP4) {
+        // the fp32 SwiGLU output, quantised per 32-block of its row
+        hipError_t err = launch_quantize_mx(ws.a, false, TK, a.F, a.offsets + a.E, ws.aq, ws.amx, st);
+        if (err != hipSuccess) return err;
+        p.act = ws.aq;
+        p.wscale = nullptr;
+        p.mx_act = ws.amx;
+        p.mx_w = static_cast<const uint8_t*>(a.sd);
+        launch_gemm<W_MXFP4, false>(p, n_items_max, path, st);
+    } else if (a.w == W_FP8) {
         hipLaunchKernelGGL(beam_quantize_a_e4m3, dim3(TK), dim3(256), 0, st, (const float*)ws.a,
                            a.offsets, a.E, a.F, ws.aq, ws.ascale);
         p.act = ws.aq;

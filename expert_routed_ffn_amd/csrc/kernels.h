@@ -38,19 +38,19 @@ struct PermuteArgs {
 size_t permute_ws_bytes(int T, int K, int E);
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t st);
 
-enum WKind { W_F32 = 0, W_BF16 = 1, W_FP8 = 2 };
+enum WKind { W_F32 = 0, W_BF16 = 1, W_FP8 = 2, W_MXFP4 = 3 };
 
 struct ExpertsArgs {
     int T, K, E, H, F;
     WKind w;
-    const void* x;          // F32 / BF16 activations or e4m3 codes
-    const float* xscale;    // FP8 only
+    const void* x;          // F32 / BF16 activations, e4m3 codes or packed E2M1 codes
+    const void* xscale;     // FP8: fp32 per token; MXFP4: E8M0 per 32-block
     const int32_t* offsets;
     const int32_t* row_token;
     const void* wgu;
-    const float* sgu;
+    const void* sgu;        // FP8: fp32 per row; MXFP4: E8M0 per 32-block
     const void* wd;
-    const float* sd;
+    const void* sd;
     void* y;
     bool y_bf16;
     void* ws;
@@ -61,6 +61,12 @@ hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st);
 // Reorders `rows` rows of `kb` bytes (rows % 16 == 0, kb % 256 == 0) into
 // the packed tile layout of the expert GEMM.
 hipError_t launch_pack(const void* src, void* dst, size_t rows, int kb, hipStream_t st);
+
+// MXFP4 quantisation of `rows` rows of K values (bf16 or fp32), K % 512 == 0:
+// packed E2M1 codes [rows, K/2] and E8M0 codes [rows, K/32].  With
+// `row_count` non-null only rows below *row_count are done.
+hipError_t launch_quantize_mx(const void* x, bool bf16, int rows, int K, const int32_t* row_count,
+                              uint8_t* q, uint8_t* s, hipStream_t st);
 
 struct CombineArgs {
     int T, K, H;

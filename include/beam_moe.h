@@ -53,18 +53,23 @@ typedef enum beam_status {
 typedef enum beam_dtype {
     BEAM_F32 = 0,
     BEAM_BF16 = 1,
-    BEAM_FP8_E4M3 = 2           /* OCP E4M3FN codes (uint8), max 448, no inf  */
+    BEAM_FP8_E4M3 = 2,          /* OCP E4M3FN codes (uint8), max 448, no inf  */
+    BEAM_MXFP4 = 3              /* OCP MXFP4: E2M1 codes packed two per byte  */
+                                /* (element 2i in the low nibble of byte i),  */
+                                /* with one E8M0 scale code (uint8, value     */
+                                /* 2^(code-127)) per 32 consecutive elements  */
+                                /* of a row, stored row-major [rows, K/32]    */
 } beam_dtype;
 
 /* Layer shape.  Beam: {5120, 256, 8, 4, 8, 2, 2560, 2.5f, 1e-6f}. */
 typedef struct beam_moe_cfg {
-    int32_t hidden;        /* H: multiple of 256, at most 8192                 */
+    int32_t hidden;        /* H: multiple of 256 (512 for MXFP4), at most 8192 */
     int32_t n_experts;     /* E: at most 256                                  */
     int32_t n_groups;      /* G: E % G == 0; experts [g*E/G, (g+1)*E/G) form group g */
     int32_t topk_groups;   /* groups kept per token, 1..G                     */
     int32_t topk;          /* K experts per token, 1..min(32, topk_groups*E/G)*/
     int32_t group_topn;    /* biased scores summed per group score, 1..min(4, E/G) */
-    int32_t d_ff;          /* F: multiple of 128 (256 for fp8 experts)         */
+    int32_t d_ff;          /* F: multiple of 128 (256 fp8, 512 MXFP4 experts)  */
     float routed_scale;    /* routing weights sum to this (2.5)               */
     float rms_eps;         /* RMSNorm epsilon (1e-6)                           */
 } beam_moe_cfg;
@@ -129,6 +134,26 @@ beam_status beam_moe_permute(const beam_moe_cfg* cfg, int32_t T,
                              void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * beam_moe_quantize_mx -- run-time MXFP4 quantisation of the layer input for
+ * the 4-bit experts.  (TokenSpeed blog, "TensorRT-LLM NVFP4 MoE": the 4-bit
+ * MoE quantises its input at run time, a step independent of the routes
+ * that may run on a second stream alongside the router; OCP Microscaling
+ * Formats (MX) v1.0: shared exponent floor(log2(amax)) - 2 per block of 32,
+ * elements rounded to the nearest E2M1 value, ties to even, saturating.)
+ *
+ *   x        [T,H] BF16 or F32 (x_dtype)
+ *   x_q      [T,H/2] out: E2M1 codes, element 2i in the low nibble of byte i
+ *   x_scale  [T,H/32] out: E8M0 scale codes; block b covers elements
+ *            [32b, 32b+32) of its row; an all-zero block gets code 0
+ * Requires hidden % 512 == 0.  E2M1 has no NaN or infinity: NaN and +-Inf
+ * elements are stored as +-6, and a block holding +-Inf gets some in-range
+ * scale code (no fault, no hang; the token's routing weights still carry
+ * the NaN of its router logits).
+ */
+beam_status beam_moe_quantize_mx(const beam_moe_cfg* cfg, int32_t T, const void* x, beam_dtype x_dtype,
+                                 uint8_t* x_q, uint8_t* x_scale, void* stream);
+
+/*
  * beam_moe_experts -- grouped SwiGLU expert MLP over the permuted rows.
  * (TokenSpeed blog, "TensorRT-LLM NVFP4 MoE": GEMM1 with SwiGLU fused,
  *  then GEMM2; Gaudi cookbook, "What was built" and "EP vs TP quality":
@@ -143,21 +168,31 @@ beam_status beam_moe_permute(const beam_moe_cfg* cfg, int32_t T,
  *             beam_moe_permute; weights are e4m3 codes with per-output-row
  *             fp32 scales; a is re-quantised per row over all F columns
  *             (scale amax/448) before GEMM2.
- *   x         [T,H] dtype per w_dtype (x_dtype must be F32, BF16 or FP8_E4M3
- *             to match); x_scale [T] fp32 iff FP8
+ *             MXFP4: the 4-bit experts (TokenSpeed blog, "NVFP4 and FP8
+ *             checkpoints": 4-bit E2M1 expert weights with block scales,
+ *             re-encoded here as OCP MXFP4); x is x_q / x_scale from
+ *             beam_moe_quantize_mx; the fp32 SwiGLU output a is quantised
+ *             the same way (32-element blocks) before GEMM2; all products on
+ *             the scaled FP4 x FP4 matrix cores, fp32 accumulation.
+ *             Supported for up to 255 rows per expert on average
+ *             (T*K < 256*E); larger calls return BEAM_ERR_UNSUPPORTED.
+ *   x         [T,H] dtype per w_dtype (x_dtype must be F32, BF16, FP8_E4M3
+ *             or MXFP4 to match; MXFP4: [T,H/2] bytes); x_scale: FP8 [T]
+ *             fp32, MXFP4 [T,H/32] E8M0 codes, else unused
  *   expert_offsets [E+1], row_token [T*K] from beam_moe_permute
- *   w_gate_up [E,2F,H]: rows [0,F) gate, [F,2F) up; s_gate_up [E,2F] iff FP8
- *   w_down    [E,H,F];                               s_down [E,H] iff FP8
+ *   w_gate_up [E,2F,H]: rows [0,F) gate, [F,2F) up; s_gate_up FP8 [E,2F]
+ *             fp32, MXFP4 [E,2F,H/32] E8M0 codes
+ *   w_down    [E,H,F]; s_down FP8 [E,H] fp32, MXFP4 [E,H,F/32] E8M0 codes
  *             Both weight stacks must be the output of beam_moe_pack_weights
  *             (same size, tiled layout); the scales stay row-major.
  *   y         [T*K,H] out, dtype y_dtype (F32 or BF16): unweighted expert
  *             outputs in permuted row order
  */
 beam_status beam_moe_experts(const beam_moe_cfg* cfg, int32_t T, beam_dtype w_dtype,
-                             const void* x, beam_dtype x_dtype, const float* x_scale,
+                             const void* x, beam_dtype x_dtype, const void* x_scale,
                              const int32_t* expert_offsets, const int32_t* row_token,
-                             const void* w_gate_up, const float* s_gate_up,
-                             const void* w_down, const float* s_down,
+                             const void* w_gate_up, const void* s_gate_up,
+                             const void* w_down, const void* s_down,
                              void* y, beam_dtype y_dtype,
                              void* ws, size_t ws_bytes, void* stream);
 
@@ -185,10 +220,10 @@ beam_status beam_moe_experts(const beam_moe_cfg* cfg, int32_t T, beam_dtype w_dt
  *     are safe.
  */
 beam_status beam_moe_experts_static(const beam_moe_cfg* cfg, int32_t T, beam_dtype w_dtype,
-                                    const void* x, beam_dtype x_dtype, const float* x_scale,
+                                    const void* x, beam_dtype x_dtype, const void* x_scale,
                                     const int32_t* expert_offsets, const int32_t* row_token,
-                                    const void* w_gate_up, const float* s_gate_up,
-                                    const void* w_down, const float* s_down,
+                                    const void* w_gate_up, const void* s_gate_up,
+                                    const void* w_down, const void* s_down,
                                     void* y, beam_dtype y_dtype, void* stream);
 
 /*
@@ -229,6 +264,8 @@ beam_status beam_moe_combine_norm(const beam_moe_cfg* cfg, int32_t T,
  *   n_experts       number of expert matrices in each stack (may be a
  *                   subset of cfg->n_experts, to pack expert by expert)
  *   w_gate_up       [n_experts,2F,H] row-major in; w_down [n_experts,H,F]
+ *                   (MXFP4: the packed E2M1 bytes, K/2 per row; the E8M0
+ *                   scales are not re-laid out)
  *   packed_gate_up, packed_down: outputs of the same byte sizes; they must
  *                   not overlap the inputs or each other.
  * (Layout choice for MI355X HBM: every weight load instruction of the

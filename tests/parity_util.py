@@ -23,6 +23,10 @@ NEAR_TIE = 1e-6
 W_RTOL = 1e-5
 BF16_MAXABS, BF16_RELL2 = 2e-2, 5e-3
 FP8_RELL2 = 3e-2
+# 4-bit (MXFP4) experts: the benchmark spec states no bound for them; the
+# quantised-path bound of the fp8 experts (rel-L2 3e-2 against the oracle
+# of the same quantised arithmetic) is taken for them too
+MX_RELL2 = 3e-2
 F32_MAXABS, F32_RELL2 = 1e-4, 1e-5
 
 
@@ -64,7 +68,7 @@ def report_over(name, got, ref, bound):
 
 
 def check_output(name, got, ref, kind):
-    """kind: 'bf16', 'fp8' or 'f32'.  Returns (max_abs, rel_l2)."""
+    """kind: 'bf16', 'fp8', 'mx' or 'f32'.  Returns (max_abs, rel_l2)."""
     ma, rl = max_abs(got, ref), rel_l2(got, ref)
     say(f"  {name}: max_abs={ma:.3e} rel_l2={rl:.3e} ({kind}, {np.size(ref)} elements)")
     if kind == "bf16" and ma > BF16_MAXABS:
@@ -73,6 +77,8 @@ def check_output(name, got, ref, kind):
         assert ma <= BF16_MAXABS and rl <= BF16_RELL2, (name, ma, rl)
     elif kind == "fp8":
         assert rl <= FP8_RELL2, (name, rl)
+    elif kind == "mx":
+        assert rl <= MX_RELL2, (name, rl)
     else:
         assert ma <= F32_MAXABS and rl <= F32_RELL2, (name, ma, rl)
     return ma, rl

@@ -2,7 +2,8 @@
 combine_norm, in the launch configuration the bench times) against the CPU
 oracle, for every workload: the tiny all-fp32 layer in full, and the Beam
 shapes (T = 8, 64 skewed, 2048 prefill, 16384 with bf16 and with fp8
-experts) with all 256 experts resident.
+experts; T = 8 and 64 with 4-bit MXFP4 experts) with all 256 experts
+resident.
 
 Per workload:
   * routing of every token (ids exact outside near-ties, weights 1e-5);
@@ -16,9 +17,10 @@ Per workload:
   * the layer outputs m, h', x_next of all tokens (T <= 64) or of a seeded
     sample of at least 32 tokens that includes tokens whose pairs sit in
     rows 64..127 of their work items;
-  * for fp8 experts also the W8A8 "floor" (W8A8 oracle against the
-    unquantised-activation oracle on the same weights), printed beside the
-    GPU's parity.
+  * for fp8 and MXFP4 experts also the quantisation "floor" (the quantised
+    oracle against the unquantised-activation oracle on the same weights),
+    printed beside the GPU's parity; the run-time activation codes are
+    compared bit for bit.
 """
 
 import numpy as np
@@ -53,6 +55,7 @@ def expert_weights_fn(wl):
     """Plain row-major weights of expert e for the oracle, regenerated per
     expert (a progress line every 32 experts)."""
     fp8 = wl.w_dtype == "fp8"
+    mx = wl.w_dtype == "mxfp4"
     calls = [0]
 
     def ew(e):
@@ -62,6 +65,9 @@ def expert_weights_fn(wl):
         a, b, c, d = synth.make_expert(wl, e, DEV)
         if fp8:
             return {"q_gu": a.cpu().numpy(), "s_gu": synth.to_f64(c), "q_d": b.cpu().numpy(), "s_d": synth.to_f64(d)}
+        if mx:
+            return {"c_gu": oracle.unpack_fp4(a.cpu().numpy()), "s_gu": c.cpu().numpy(),
+                    "c_d": oracle.unpack_fp4(b.cpu().numpy()), "s_d": d.cpu().numpy()}
         return {"w_gu": synth.to_f64(a), "w_d": synth.to_f64(b)}
     return ew
 
@@ -111,7 +117,9 @@ def run_layer(wname, n_sample, check_experts=True):
     w_r, bias = synth.make_router(wl, DEV)
     x, h, gp, gq = synth.make_activations(wl, DEV)
     fp8 = wl.w_dtype == "fp8"
-    w_dt = {"f32": beam.BEAM_F32, "bf16": beam.BEAM_BF16, "fp8": beam.BEAM_FP8_E4M3}[wl.w_dtype]
+    mx = wl.w_dtype == "mxfp4"
+    w_dt = {"f32": beam.BEAM_F32, "bf16": beam.BEAM_BF16, "fp8": beam.BEAM_FP8_E4M3,
+            "mxfp4": beam.BEAM_MXFP4}[wl.w_dtype]
     y_dt = torch.bfloat16 if fp8 else torch.float32
     bufs = beam.alloc_buffers(cfg, wl.T, x.dtype, w_dt, y_dtype=y_dt, keep_logits=True,
                               keep_moe_out=True, device=DEV)
@@ -148,8 +156,13 @@ def run_layer(wname, n_sample, check_experts=True):
         for t in sample_tokens(wl.T, 64, seed=1):
             s, q = oracle.quantize_row_e4m3(xn[t])
             assert s_gpu[t] == s and np.array_equal(q_gpu[t], q), t
+    if mx:
+        # run-time MXFP4 codes and block scales of x, bit for bit
+        s_o, q_o = oracle.quantize_mx_fp4(xn)
+        np.testing.assert_array_equal(bufs.x_scale.cpu().numpy(), s_o)
+        np.testing.assert_array_equal(oracle.unpack_fp4(bufs.x_q.cpu().numpy()), oracle.e2m1_encode(q_o))
 
-    kind = {"f32": "f32", "bf16": "bf16", "fp8": "fp8"}[wl.w_dtype]
+    kind = {"f32": "f32", "bf16": "bf16", "fp8": "fp8", "mxfp4": "mx"}[wl.w_dtype]
     ew = expert_weights_fn(wl)
     rnd = oracle.round_f32 if wl.act_dtype == "f32" else oracle.round_bf16
 
@@ -162,6 +175,8 @@ def run_layer(wname, n_sample, check_experts=True):
             u = xn[o_rt[lo:hi]]
             if fp8:
                 ref = oracle.expert_ffn_w8a8(u, w["q_gu"], w["s_gu"], w["q_d"], w["s_d"])
+            elif mx:
+                ref = oracle.expert_ffn_w4a4(u, w["c_gu"], w["s_gu"], w["c_d"], w["s_d"])
             else:
                 ref = oracle.expert_ffn(u, w["w_gu"], w["w_d"], round_a=rnd)
             got = y_gpu[lo:hi].double().cpu().numpy()
@@ -192,6 +207,20 @@ def run_layer(wname, n_sample, check_experts=True):
                                   ids_override={t: override[t] for t in differ})
         say(f"  W8A8 floor (W8A8 oracle vs unquantised activations): rel_l2(m)={rel_l2(ref['m'], flo['m']):.3e}; "
             f"GPU vs W8A8 oracle rel_l2(m)={rel_l2(bufs.moe_out.cpu().double().numpy()[tokens], ref['m']):.3e}")
+    if mx:
+        # the 4-bit floor: W4A4 oracle against unquantised activations on the
+        # same dequantised weights
+        def ew_float(e):
+            w = ew(e)
+            def deq(c, sc):
+                return oracle.e2m1_decode(c) * np.repeat(oracle.e8m0_decode(sc), oracle.MX_BLOCK, axis=-1)
+            return {"w_gu": deq(w["c_gu"], w["s_gu"]), "w_d": deq(w["c_d"], w["s_d"])}
+        flo = oracle.layer_tokens(ocfg, xn, synth.to_f64(w_r), synth.to_f64(bias), ew_float,
+                                  synth.to_f64(h), synth.to_f64(gp), synth.to_f64(gq), wl.n,
+                                  tokens=tokens, w_dtype="bf16", rnd=lambda v: np.asarray(v, np.float64),
+                                  ids_override={t: override[t] for t in differ})
+        say(f"  W4A4 floor (W4A4 oracle vs unquantised activations): rel_l2(m)={rel_l2(ref['m'], flo['m']):.3e}; "
+            f"GPU vs W4A4 oracle rel_l2(m)={rel_l2(bufs.moe_out.cpu().double().numpy()[tokens], ref['m']):.3e}")
     return n_near
 
 
@@ -320,6 +349,14 @@ def test_layer_prefill_bf16_t16384():
 @pytest.mark.timeout(400)
 def test_layer_prefill_fp8_t16384():
     run_layer("prefill_fp8_t16384", 32)
+
+
+def test_layer_decode_t8_mxfp4():
+    run_layer("decode_t8_mxfp4", 8)
+
+
+def test_layer_skew_t64_mxfp4():
+    run_layer("skew_t64_mxfp4", 64)
 
 
 def test_layer_special_rows_fp8():

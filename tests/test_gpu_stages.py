@@ -161,14 +161,20 @@ def _run_experts_stage(wl, T, ids_np, y_dtype):
     E, K = wl.n_experts, wl.topk
     wgu, wd, sgu, sd = synth.make_expert_stacks(wl, DEV)
     pgu, pd = torch.empty_like(wgu), torch.empty_like(wd)
-    beam.beam_moe_pack_weights(cfg, wgu, wd, pgu, pd)
+    mx = wl.w_dtype == "mxfp4"
+    beam.beam_moe_pack_weights(cfg, wgu, wd, pgu, pd, mxfp4=mx)
     x, _, _, _ = synth.make_activations(wl, DEV, T=T)
     o_off, o_rt, _ = oracle.permutation(ids_np, E)
     off = torch.from_numpy(o_off.astype(np.int32)).to(DEV)
     rt = torch.from_numpy(o_rt.astype(np.int32)).to(DEV)
     y = torch.empty((T * K, wl.hidden), dtype=y_dtype, device=DEV)
-    ws = beam.workspace(cfg, T, beam._dt(wgu))
-    if wl.w_dtype == "fp8":
+    ws = beam.workspace(cfg, T, beam.BEAM_MXFP4 if mx else beam._dt(wgu))
+    if mx:
+        xq = torch.empty((T, wl.hidden // 2), dtype=torch.uint8, device=DEV)
+        xs = torch.empty((T, wl.hidden // 32), dtype=torch.uint8, device=DEV)
+        beam.beam_moe_quantize_mx(cfg, x, xq, xs)
+        beam.beam_moe_experts(cfg, T, xq, off, rt, pgu, pd, y, x_scale=xs, s_gate_up=sgu, s_down=sd, ws=ws)
+    elif wl.w_dtype == "fp8":
         xq = torch.empty((T, wl.hidden), dtype=torch.uint8, device=DEV)
         xs = torch.empty(T, dtype=torch.float32, device=DEV)
         ids = torch.from_numpy(ids_np.astype(np.int32)).to(DEV)
@@ -189,6 +195,9 @@ def _run_experts_stage(wl, T, ids_np, y_dtype):
         if wl.w_dtype == "fp8":
             ref[lo:hi] = oracle.expert_ffn_w8a8(u, wgu[e].cpu().numpy(), synth.to_f64(sgu[e]),
                                                 wd[e].cpu().numpy(), synth.to_f64(sd[e]))
+        elif mx:
+            ref[lo:hi] = oracle.expert_ffn_w4a4(u, oracle.unpack_fp4(wgu[e].cpu().numpy()), sgu[e].cpu().numpy(),
+                                                oracle.unpack_fp4(wd[e].cpu().numpy()), sd[e].cpu().numpy())
         else:
             rnd = oracle.round_f32 if wl.w_dtype == "f32" else oracle.round_bf16
             ref[lo:hi] = oracle.expert_ffn(u, synth.to_f64(wgu[e]), synth.to_f64(wd[e]), round_a=rnd)
@@ -222,6 +231,43 @@ def test_experts_parity(w_dtype, y_dtype, T, skew):
     check_output("y", got, ref, kind)
     if kind == "bf16":
         assert rel_l2(got, ref) < 2e-3
+
+
+@pytest.mark.parametrize("y_dtype,T,skew", [
+    (torch.float32, 5, 0.0),       # <= 16 tokens: the direct kernel
+    (torch.bfloat16, 12, 0.0),
+    (torch.float32, 300, 0.5),     # 128-row items staged in LDS, ragged tails
+    (torch.float32, 37, 3.0),      # heavy skew, empty experts
+])
+def test_experts_mxfp4_parity(y_dtype, T, skew):
+    say(f"experts mxfp4 y={y_dtype} T={T} skew={skew}")
+    wl = _stage_wl("mxfp4", H=512, F=512)
+    ids = synth.random_ids(T, wl.n_experts, wl.topk, skew=skew).numpy()
+    got, ref = _run_experts_stage(wl, T, ids, y_dtype)
+    check_output("y", got, ref, "mx")
+
+
+def test_quantize_mx_bit_exact():
+    say("run-time MXFP4 quantisation of x")
+    T, H = 37, 5120
+    g = torch.Generator(device=DEV).manual_seed(5)
+    scale = torch.logspace(-3, 3, T, device=DEV).unsqueeze(1)
+    x = torch.randn((T, H), generator=g, device=DEV) * scale
+    x[5] = 0.0                                             # all-zero row
+    x[6] = x[6] * torch.logspace(-6, 0, H, device=DEV)     # wide range inside a row
+    x[7, :32] = 0.0                                        # one all-zero block
+    # E2M1 ties: block max 6 * 2^-1 = 3 (scale 2^-1), then ties at 0.25, 0.75, ... x 2^-1
+    x[8, :32] = torch.tensor([3.0] + [0.125, 0.375, 0.625, 0.875, 1.25, 1.75, 2.5] * 4 + [0.0] * 3, device=DEV)
+    for xdt in (torch.bfloat16, torch.float32):
+        xx = x.to(xdt)
+        cfg = beam.LayerCfg()
+        xq = torch.empty((T, H // 2), dtype=torch.uint8, device=DEV)
+        xs = torch.empty((T, H // 32), dtype=torch.uint8, device=DEV)
+        beam.beam_moe_quantize_mx(cfg, xx, xq, xs)
+        torch.cuda.synchronize()
+        s_o, q_o = oracle.quantize_mx_fp4(synth.to_f64(xx))
+        np.testing.assert_array_equal(xs.cpu().numpy(), s_o)
+        np.testing.assert_array_equal(oracle.unpack_fp4(xq.cpu().numpy()), oracle.e2m1_encode(q_o))
 
 
 def test_experts_every_token_on_one_expert():
