@@ -41,6 +41,7 @@ __all__ = [
     "norm_boundary", "layer_tokens", "E4M3_MAX",
     "E2M1_MAX", "MX_BLOCK", "e2m1_decode", "e2m1_round", "e2m1_encode", "e8m0_decode",
     "quantize_mx_fp4", "unpack_fp4", "expert_ffn_w4a4",
+    "dense_layer_tokens", "combine_shard",
 ]
 
 E4M3_MAX = 448.0
@@ -481,6 +482,46 @@ def norm_boundary(m, h, gamma_post, gamma_pre, n, eps, rnd=round_bf16):
     h_new = rnd(math.sqrt((n - 1) / n) * np.asarray(h, np.float64) + p / math.sqrt(n))
     x_next = rnd(rmsnorm(h_new, gamma_pre, eps))
     return p, h_new, x_next
+
+
+# --------------------------------------------------------------------------
+# the dense layers and one expert-parallel shard
+# --------------------------------------------------------------------------
+
+def dense_layer_tokens(cfg, x, w_gu, w_d, h, gamma_post, gamma_pre, n, tokens=None, rnd=round_bf16):
+    """A dense layer's MLP and its sandwich-norm boundary, for the listed tokens.
+
+    The first three layers use a dense SwiGLU MLP with d_ff 20480 instead of
+    the MoE ([VL] MoE section; [TS] "Architecture": three dense layers, then
+    49 MoE layers), with the same norm before and after every block
+    ([TS] "Architecture": SandwichNorm and depth-scaled residuals).  Reading:
+    the MLP is the expert MLP of this module over all tokens (a = silu(g) * v
+    rounded by rnd, output unrounded) and its output takes the place of the
+    MoE output m in the boundary.  Returns dict with y (= m), p, h_new, x_next.
+    """
+    x = np.asarray(x, np.float64)
+    tokens = list(range(x.shape[0])) if tokens is None else list(tokens)
+    y = expert_ffn(x[tokens], w_gu, w_d, round_a=rnd)
+    p, hn, xn = norm_boundary(y, np.asarray(h, np.float64)[tokens], gamma_post, gamma_pre, n,
+                              cfg["rms_eps"], rnd)
+    return {"tokens": tokens, "y": y, "p": p, "h_new": hn, "x_next": xn}
+
+
+def combine_shard(y, ids, w, expert_begin, n_local):
+    """One expert-parallel shard's part of a token's combine: the weighted
+    sum over the token's experts in [expert_begin, expert_begin + n_local).
+
+    Under EP8 each GPU holds 32 complete experts, processes the tokens routed
+    to them and an all-reduce sums the partial MoE outputs; normalisation
+    runs after it ([TS] "Tensor parallelism and expert parallelism"; [GD]
+    "At a glance": EP 8, 32 experts per card).  The shards' partial sums add
+    up to combine(y, w).
+    """
+    y = np.asarray(y, np.float64)
+    ids = np.asarray(ids)
+    keep = (ids >= expert_begin) & (ids < expert_begin + n_local)
+    w = np.where(keep, np.asarray(w, np.float64), 0.0)
+    return (w[:, None] * y).sum(axis=0)
 
 
 # --------------------------------------------------------------------------

@@ -49,6 +49,7 @@ class Workload:
     zipf_s: float = 0.0      # >0: add a Zipf(s) per-expert offset spanning +-0.5
     token_lognormal: float = 0.0  # >0: scale each x row by LogNormal(0, this)
     seed: int = 0
+    dense: bool = False      # a dense SwiGLU layer (one MLP of width d_ff over all tokens)
 
     def with_T(self, T: int) -> "Workload":
         return dataclasses.replace(self, T=T)
@@ -77,6 +78,15 @@ WORKLOADS = {
                                 bias_sigma=0.02, seed=1, **_BEAM),
     "skew_t64_mxfp4": Workload("skew_t64_mxfp4", T=64, n=20, act_dtype="bf16", w_dtype="mxfp4",
                                bias_sigma=0.02, zipf_s=1.1, seed=1, **_BEAM),
+    # the dense layers (0-2): one SwiGLU MLP of width 20480 over all tokens,
+    # bf16 weights, the same norm boundary
+    "dense_t8": Workload("dense_t8", T=8, hidden=5120, n_experts=1, n_groups=1, topk_groups=1, topk=1,
+                         group_topn=1, d_ff=20480, routed_scale=1.0, rms_eps=1e-6, n=2, act_dtype="bf16",
+                         w_dtype="bf16", bias_sigma=0.0, seed=2, dense=True),
+    "dense_t2048": Workload("dense_t2048", T=2048, hidden=5120, n_experts=1, n_groups=1, topk_groups=1,
+                            topk=1, group_topn=1, d_ff=20480, routed_scale=1.0, rms_eps=1e-6, n=2,
+                            act_dtype="bf16", w_dtype="bf16", bias_sigma=0.0, token_lognormal=0.5, seed=2,
+                            dense=True),
     # the fp8 prefill shape with the bf16 experts of the other Beam workloads:
     # about 512 rows per expert, past the point where bf16 matrix-core
     # throughput rather than HBM bandwidth bounds the expert GEMMs
@@ -84,9 +94,10 @@ WORKLOADS = {
                                     w_dtype="bf16", bias_sigma=0.02, seed=1, **_BEAM),
 }
 # the order the workloads are listed in (index = position in that list; the
-# bf16 16384-token shape and the 4-bit decode shapes came after the first five)
+# bf16 16384-token shape, the 4-bit decode shapes and the dense layers came
+# after the first five)
 WORKLOAD_ORDER = ["tiny_fp32", "decode_t8", "skew_t64", "prefill_t2048", "prefill_fp8_t16384",
-                  "prefill_bf16_t16384", "decode_t8_mxfp4", "skew_t64_mxfp4"]
+                  "prefill_bf16_t16384", "decode_t8_mxfp4", "skew_t64_mxfp4", "dense_t8", "dense_t2048"]
 
 
 def _seed(*parts: int) -> int:

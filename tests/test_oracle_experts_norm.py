@@ -244,3 +244,49 @@ def test_w8a8_rows_are_independent():
     full = oracle.expert_ffn_w8a8(u, q_gu, s_gu, q_d, s_d)
     for r in range(5):
         np.testing.assert_array_equal(full[r], oracle.expert_ffn_w8a8(u[r], q_gu, s_gu, q_d, s_d)[0])
+
+
+def test_dense_layer_matches_torch_swiglu_and_boundary():
+    # the dense MLP against torch's own linear / silu at a d_ff several times
+    # the hidden size, then the boundary on its output
+    rng = np.random.default_rng(9)
+    H, F, T = 64, 320, 3
+    x = rng.standard_normal((T, H))
+    w_gu = rng.standard_normal((2 * F, H)) / math.sqrt(H)
+    w_d = rng.standard_normal((H, F)) / math.sqrt(F)
+    h = rng.standard_normal((T, H))
+    gp, gq = 1 + 0.1 * rng.standard_normal(H), 1 + 0.1 * rng.standard_normal(H)
+    cfg = {"rms_eps": 1e-6}
+    out = oracle.dense_layer_tokens(cfg, x, w_gu, w_d, h, gp, gq, 3, rnd=ident)
+    lin = torch.nn.functional.linear
+    tx = torch.from_numpy(x)
+    y = lin(torch.nn.functional.silu(lin(tx, torch.from_numpy(w_gu[:F]))) * lin(tx, torch.from_numpy(w_gu[F:])),
+            torch.from_numpy(w_d)).numpy()
+    np.testing.assert_allclose(out["y"], y, rtol=1e-12, atol=1e-13)
+    rms = torch.nn.functional.rms_norm(torch.from_numpy(y), (H,), torch.from_numpy(gp), eps=1e-6).numpy()
+    np.testing.assert_allclose(out["p"], rms, rtol=1e-12, atol=1e-13)
+    hn = math.sqrt(2 / 3) * h + rms / math.sqrt(3)
+    np.testing.assert_allclose(out["h_new"], hn, rtol=1e-12, atol=1e-13)
+    xn = torch.nn.functional.rms_norm(torch.from_numpy(hn), (H,), torch.from_numpy(gq), eps=1e-6).numpy()
+    np.testing.assert_allclose(out["x_next"], xn, rtol=1e-12, atol=1e-13)
+
+
+def test_shard_partials_sum_to_the_combine():
+    # 8 contiguous shards of 32 experts partition every token's K experts:
+    # their partial sums add up to the full combine, a shard without the
+    # token's experts contributes zero, and each partial is the combine of
+    # exactly its own experts
+    rng = np.random.default_rng(10)
+    K, H = 8, 16
+    for _ in range(20):
+        ids = rng.choice(256, K, replace=False)
+        w = rng.uniform(0.1, 1, K)
+        y = rng.standard_normal((K, H))
+        parts = [oracle.combine_shard(y, ids, w, 32 * r, 32) for r in range(8)]
+        np.testing.assert_allclose(sum(parts), oracle.combine(y, w), rtol=1e-13, atol=1e-14)
+        for r in range(8):
+            own = (ids >= 32 * r) & (ids < 32 * r + 32)
+            if not own.any():
+                assert np.all(parts[r] == 0)
+            else:
+                np.testing.assert_allclose(parts[r], oracle.combine(y[own], w[own]), rtol=1e-13, atol=1e-14)
