@@ -29,8 +29,10 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape or dtype",
           3: "workspace missing or too small", 4: "HIP launch failed"}
 
 SYMBOLS = ("beam_moe_route", "beam_moe_permute", "beam_moe_quantize_mx", "beam_moe_experts",
-           "beam_moe_experts_static", "beam_moe_combine_norm", "beam_moe_pack_weights",
-           "beam_moe_workspace_bytes", "beam_moe_status_string")
+           "beam_moe_experts_static", "beam_moe_combine_norm", "beam_moe_norm_boundary",
+           "beam_moe_permute_shard", "beam_moe_combine_partial", "beam_moe_dense_mlp",
+           "beam_moe_dense_workspace_bytes", "beam_moe_pack_weights", "beam_moe_workspace_bytes",
+           "beam_moe_status_string")
 STATIC_SCRATCH_BYTES = 64 << 20   # BEAM_MOE_STATIC_SCRATCH_BYTES
 
 
@@ -86,6 +88,12 @@ def lib() -> ctypes.CDLL:
                                    vp, sz, vp]
     L.beam_moe_experts_static.argtypes = [cfgp, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp]
     L.beam_moe_quantize_mx.argtypes = [cfgp, i32, vp, i32, vp, vp, vp]
+    L.beam_moe_norm_boundary.argtypes = [cfgp, i32, vp, i32, vp, vp, i32, vp, vp, i32, vp]
+    L.beam_moe_permute_shard.argtypes = [cfgp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    L.beam_moe_combine_partial.argtypes = [cfgp, i32, vp, i32, vp, vp, vp, vp]
+    L.beam_moe_dense_mlp.argtypes = [cfgp, i32, i32, vp, i32, vp, vp, vp, vp, sz, vp]
+    L.beam_moe_dense_workspace_bytes.argtypes = [cfgp, i32, i32]
+    L.beam_moe_dense_workspace_bytes.restype = sz
     L.beam_moe_combine_norm.argtypes = [cfgp, i32, vp, i32, vp, vp, vp, vp, i32, vp, vp, i32, vp, vp]
     L.beam_moe_pack_weights.argtypes = [cfgp, i32, i32, vp, vp, vp, vp, vp]
     L.beam_moe_workspace_bytes.argtypes = [cfgp, i32, i32]
@@ -93,7 +101,9 @@ def lib() -> ctypes.CDLL:
     L.beam_moe_status_string.argtypes = [i32]
     L.beam_moe_status_string.restype = ctypes.c_char_p
     for f in ("beam_moe_route", "beam_moe_permute", "beam_moe_quantize_mx", "beam_moe_experts",
-              "beam_moe_experts_static", "beam_moe_combine_norm", "beam_moe_pack_weights"):
+              "beam_moe_experts_static", "beam_moe_combine_norm", "beam_moe_norm_boundary",
+              "beam_moe_permute_shard", "beam_moe_combine_partial", "beam_moe_dense_mlp",
+              "beam_moe_pack_weights"):
         getattr(L, f).restype = i32
     _lib = L
     return L
@@ -275,6 +285,68 @@ def beam_moe_combine_norm(cfg: LayerCfg, y, pair_row, topk_w, h, x_next, gamma_p
                                      _p(topk_w), _p(h), _p(x_next), _dt(h), _p(gamma_post),
                                      _p(gamma_pre), int(n), _p(moe_out), _stream(stream))
     _ok("beam_moe_combine_norm", st)
+
+
+def beam_moe_norm_boundary(cfg: LayerCfg, m, h, x_next, gamma_post, gamma_pre, n, stream=None):
+    """Sandwich-norm boundary on a given m [T,H] (fp32/bf16): h updated in
+    place, x_next written."""
+    T, H = h.shape[0], cfg.hidden
+    _check(m, (T, H), (torch.float32, torch.bfloat16), "m")
+    _check(h, (T, H), (torch.float32, torch.bfloat16), "h")
+    _check(x_next, (T, H), (h.dtype,), "x_next")
+    _check(gamma_post, (H,), (h.dtype,), "gamma_post")
+    _check(gamma_pre, (H,), (h.dtype,), "gamma_pre")
+    st = lib().beam_moe_norm_boundary(ctypes.byref(cfg.c()), T, _p(m), _dt(m), _p(h), _p(x_next), _dt(h),
+                                      _p(gamma_post), _p(gamma_pre), int(n), _stream(stream))
+    _ok("beam_moe_norm_boundary", st)
+
+
+def beam_moe_permute_shard(cfg: LayerCfg, topk_ids, expert_begin, n_local, expert_offsets, row_token, pair_row,
+                           ws=None, stream=None):
+    """Stable grouping of the pairs routed to experts [expert_begin,
+    expert_begin + n_local); other pairs get pair_row -1."""
+    T = topk_ids.shape[0]
+    TK = T * cfg.topk
+    _check(topk_ids, (T, cfg.topk), (torch.int32,), "topk_ids")
+    _check(expert_offsets, (n_local + 1,), (torch.int32,), "expert_offsets")
+    _check(row_token, (TK,), (torch.int32,), "row_token")
+    _check(pair_row, (TK,), (torch.int32,), "pair_row")
+    st = lib().beam_moe_permute_shard(ctypes.byref(cfg.c()), T, int(expert_begin), int(n_local), _p(topk_ids),
+                                      _p(expert_offsets), _p(row_token), _p(pair_row), _p(ws),
+                                      0 if ws is None else ws.numel(), _stream(stream))
+    _ok("beam_moe_permute_shard", st)
+
+
+def beam_moe_combine_partial(cfg: LayerCfg, y, pair_row, topk_w, m_out, stream=None):
+    """One shard's share of the weighted combine (fp32, no norm)."""
+    T = topk_w.shape[0]
+    H, TK = cfg.hidden, T * cfg.topk
+    _check(y, (TK, H), (torch.float32, torch.bfloat16), "y")
+    _check(pair_row, (TK,), (torch.int32,), "pair_row")
+    _check(topk_w, (T, cfg.topk), (torch.float32,), "topk_w")
+    _check(m_out, (T, H), (torch.float32,), "m_out")
+    st = lib().beam_moe_combine_partial(ctypes.byref(cfg.c()), T, _p(y), _dt(y), _p(pair_row), _p(topk_w),
+                                        _p(m_out), _stream(stream))
+    _ok("beam_moe_combine_partial", st)
+
+
+def dense_workspace(cfg: LayerCfg, T: int, d_ff: int, device="cuda") -> torch.Tensor:
+    n = int(lib().beam_moe_dense_workspace_bytes(ctypes.byref(cfg.c()), T, d_ff))
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def beam_moe_dense_mlp(cfg: LayerCfg, x, w_gate_up, w_down, y, ws, stream=None):
+    """Dense SwiGLU MLP of width d_ff = w_gate_up.shape[0] // 2 over all rows
+    of x [T,H] bf16; packed weights; y [T,H] fp32."""
+    T, H = x.shape[0], cfg.hidden
+    Fd = w_gate_up.shape[0] // 2
+    _check(x, (T, H), (torch.bfloat16,), "x")
+    _check(w_gate_up, (2 * Fd, H), (torch.bfloat16,), "w_gate_up")
+    _check(w_down, (H, Fd), (torch.bfloat16,), "w_down")
+    _check(y, (T, H), (torch.float32,), "y")
+    st = lib().beam_moe_dense_mlp(ctypes.byref(cfg.c()), T, Fd, _p(x), BEAM_BF16, _p(w_gate_up), _p(w_down),
+                                  _p(y), _p(ws), ws.numel(), _stream(stream))
+    _ok("beam_moe_dense_mlp", st)
 
 
 def beam_moe_pack_weights(cfg: LayerCfg, w_gate_up, w_down, packed_gate_up, packed_down, stream=None,

@@ -17,6 +17,7 @@ static __device__ __align__(256) uint8_t scratch[BEAM_MOE_STATIC_SCRATCH_BYTES];
 namespace {
 
 constexpr int64_t kMaxT = 1 << 22;   // T*K stays far below 2^31
+constexpr int kMaxDenseFF = 32768;  // widest dense MLP (the dense layers use 20480)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -66,6 +67,27 @@ beam::WKind wkind(beam_dtype d) {
 
 // 4-bit experts: rows of K values are K/2 bytes in whole 256-byte chunks
 bool mx_shape_ok(const beam_moe_cfg* c) { return c->hidden % 512 == 0 && c->d_ff % 512 == 0; }
+
+// Dense MLP: the rows form one "expert".  At decode sizes (direct kernel)
+// the down projection is split over K so that its H/128 output tiles still
+// fill the chip: the smallest slice count >= 256 / tiles that divides the
+// 256-byte K iterations.
+int dense_ksplit(int T, int H, int Fd) {
+    if (T > 16) return 1;
+    const int tiles = H / 128, nk = Fd * 2 / 256;
+    int want = (256 + tiles - 1) / tiles;
+    for (int s = want; s <= nk; ++s)
+        if (nk % s == 0) return s;
+    return 1;
+}
+
+size_t dense_ws_bytes(int T, int H, int Fd) {
+    const int S = dense_ksplit(T, H, Fd);
+    size_t b = 256 + align256((size_t)T * sizeof(int32_t));
+    b += beam::experts_ws_bytes(T, 1, 1, H, Fd, beam::W_BF16);
+    if (S > 1) b += align256((size_t)S * T * H * sizeof(float));
+    return b;
+}
 
 // Checks of beam_moe_experts that do not concern the workspace; fills `a`
 // (all but a.ws) and the workspace bytes the call needs.
@@ -281,7 +303,7 @@ beam_status beam_moe_pack_weights(const beam_moe_cfg* cfg, int32_t n_experts, be
                                   void* packed_down, void* stream) {
     // packing only depends on the matrix shapes (hidden, d_ff)
     if (!cfg || cfg->hidden <= 0 || cfg->d_ff <= 0) return BEAM_ERR_INVALID_ARG;
-    if (cfg->hidden % 256 != 0 || cfg->hidden > 8192 || cfg->d_ff % 128 != 0 || cfg->d_ff > 8192)
+    if (cfg->hidden % 256 != 0 || cfg->hidden > 8192 || cfg->d_ff % 128 != 0 || cfg->d_ff > kMaxDenseFF)
         return BEAM_ERR_UNSUPPORTED;
     if (n_experts < 0 || !valid_dtype(w_dtype)) return BEAM_ERR_INVALID_ARG;
     if (w_dtype == BEAM_FP8_E4M3 && (cfg->hidden % 256 != 0 || cfg->d_ff % 256 != 0))
@@ -364,6 +386,138 @@ beam_status beam_moe_combine_norm(const beam_moe_cfg* cfg, int32_t T, const void
     a.c_new = (float)(1.0 / sqrt((double)n));
     a.eps = cfg->rms_eps;
     a.moe_out = moe_out;
+    return beam::launch_combine_norm(a, static_cast<hipStream_t>(stream)) == hipSuccess ? BEAM_OK
+                                                                                         : BEAM_ERR_HIP;
+}
+
+size_t beam_moe_dense_workspace_bytes(const beam_moe_cfg* cfg, int32_t T, int32_t d_ff) {
+    if (!cfg || cfg->hidden <= 0 || cfg->hidden % 256 != 0 || cfg->hidden > 8192) return 0;
+    if (T < 0 || T > kMaxT || d_ff <= 0 || d_ff % 128 != 0 || d_ff > kMaxDenseFF) return 0;
+    if (T == 0) return 256;
+    return dense_ws_bytes(T, cfg->hidden, d_ff);
+}
+
+beam_status beam_moe_dense_mlp(const beam_moe_cfg* cfg, int32_t T, int32_t d_ff, const void* x,
+                               beam_dtype x_dtype, const void* w_gate_up, const void* w_down, float* y,
+                               void* ws, size_t ws_bytes, void* stream) {
+    if (!cfg || cfg->hidden <= 0 || d_ff <= 0 || T < 0 || T > kMaxT) return BEAM_ERR_INVALID_ARG;
+    if (cfg->hidden % 256 != 0 || cfg->hidden > 8192 || d_ff % 128 != 0 || d_ff > kMaxDenseFF)
+        return BEAM_ERR_UNSUPPORTED;
+    if (x_dtype != BEAM_BF16) return BEAM_ERR_INVALID_ARG;
+    if (T == 0) return BEAM_OK;
+    if (!x || !w_gate_up || !w_down || !y) return BEAM_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(y))
+        return BEAM_ERR_INVALID_ARG;
+    const int H = cfg->hidden;
+    if (!ws || ws_bytes < dense_ws_bytes(T, H, d_ff) || !aligned16(ws)) return BEAM_ERR_WORKSPACE;
+    const int S = dense_ksplit(T, H, d_ff);
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    int32_t* offsets = reinterpret_cast<int32_t*>(base);
+    int32_t* row_token = reinterpret_cast<int32_t*>(base + 256);
+    uint8_t* ews = base + 256 + align256((size_t)T * sizeof(int32_t));
+    float* parts = S > 1 ? reinterpret_cast<float*>(ews + beam::experts_ws_bytes(T, 1, 1, H, d_ff, beam::W_BF16))
+                         : y;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (beam::launch_dense_rows(T, offsets, row_token, st) != hipSuccess) return BEAM_ERR_HIP;
+    beam::ExpertsArgs a{};
+    a.T = T;
+    a.K = 1;
+    a.E = 1;
+    a.H = H;
+    a.F = d_ff;
+    a.w = beam::W_BF16;
+    a.x = x;
+    a.offsets = offsets;
+    a.row_token = row_token;
+    a.wgu = w_gate_up;
+    a.wd = w_down;
+    a.y = parts;
+    a.y_bf16 = false;
+    a.ws = ews;
+    a.ksplit = S;
+    a.y_slice_stride = (size_t)T * H;
+    if (beam::launch_experts(a, st) != hipSuccess) return BEAM_ERR_HIP;
+    if (S > 1 && beam::launch_sum_slices(parts, S, (size_t)T * H, y, st) != hipSuccess) return BEAM_ERR_HIP;
+    return BEAM_OK;
+}
+
+beam_status beam_moe_permute_shard(const beam_moe_cfg* cfg, int32_t T, int32_t expert_begin, int32_t n_local,
+                                   const int32_t* topk_ids, int32_t* expert_offsets, int32_t* row_token,
+                                   int32_t* pair_row, void* ws, size_t ws_bytes, void* stream) {
+    beam_status st = check_cfg(cfg);
+    if (st != BEAM_OK) return st;
+    if (T < 0 || T > kMaxT) return BEAM_ERR_INVALID_ARG;
+    if (n_local <= 0 || expert_begin < 0 || expert_begin + n_local > cfg->n_experts) return BEAM_ERR_INVALID_ARG;
+    if (T == 0) return BEAM_OK;
+    if (!topk_ids || !expert_offsets || !row_token || !pair_row) return BEAM_ERR_INVALID_ARG;
+    const size_t need = beam::permute_ws_bytes(T, cfg->topk, n_local);
+    if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return BEAM_ERR_WORKSPACE;
+    beam::PermuteArgs a{};
+    a.T = T;
+    a.K = cfg->topk;
+    a.E = n_local;
+    a.e_base = expert_begin;
+    a.H = cfg->hidden;
+    a.ids = topk_ids;
+    a.offsets = expert_offsets;
+    a.row_token = row_token;
+    a.pair_row = pair_row;
+    a.ws = ws;
+    return beam::launch_permute(a, static_cast<hipStream_t>(stream)) == hipSuccess ? BEAM_OK : BEAM_ERR_HIP;
+}
+
+beam_status beam_moe_combine_partial(const beam_moe_cfg* cfg, int32_t T, const void* y, beam_dtype y_dtype,
+                                     const int32_t* pair_row, const float* topk_w, float* m_out, void* stream) {
+    beam_status st = check_cfg(cfg);
+    if (st != BEAM_OK) return st;
+    if (T < 0 || T > kMaxT) return BEAM_ERR_INVALID_ARG;
+    if (y_dtype != BEAM_F32 && y_dtype != BEAM_BF16) return BEAM_ERR_INVALID_ARG;
+    if (T == 0) return BEAM_OK;
+    if (!y || !pair_row || !topk_w || !m_out) return BEAM_ERR_INVALID_ARG;
+    if (!aligned16(y) || !aligned16(m_out)) return BEAM_ERR_INVALID_ARG;
+    beam::CombineArgs a{};
+    a.T = T;
+    a.K = cfg->topk;
+    a.H = cfg->hidden;
+    a.y = y;
+    a.y_bf16 = y_dtype == BEAM_BF16;
+    a.pair_row = pair_row;
+    a.w = topk_w;
+    a.moe_out = m_out;
+    a.partial_only = true;
+    return beam::launch_combine_norm(a, static_cast<hipStream_t>(stream)) == hipSuccess ? BEAM_OK
+                                                                                         : BEAM_ERR_HIP;
+}
+
+beam_status beam_moe_norm_boundary(const beam_moe_cfg* cfg, int32_t T, const void* m, beam_dtype m_dtype,
+                                   void* h, void* x_next, beam_dtype act_dtype, const void* gamma_post,
+                                   const void* gamma_pre, int32_t n, void* stream) {
+    if (!cfg || cfg->hidden <= 0 || cfg->hidden % 256 != 0 || cfg->hidden > 8192) return BEAM_ERR_INVALID_ARG;
+    if (!(cfg->rms_eps >= 0.f) || !isfinite(cfg->rms_eps)) return BEAM_ERR_INVALID_ARG;
+    if (T < 0 || T > kMaxT || n < 1) return BEAM_ERR_INVALID_ARG;
+    if ((m_dtype != BEAM_F32 && m_dtype != BEAM_BF16) || (act_dtype != BEAM_F32 && act_dtype != BEAM_BF16))
+        return BEAM_ERR_INVALID_ARG;
+    if (T == 0) return BEAM_OK;
+    if (!m || !h || !x_next || !gamma_post || !gamma_pre || h == x_next) return BEAM_ERR_INVALID_ARG;
+    if (!aligned16(m) || !aligned16(h) || !aligned16(x_next) || !aligned16(gamma_post) || !aligned16(gamma_pre))
+        return BEAM_ERR_INVALID_ARG;
+    beam::CombineArgs a{};
+    a.T = T;
+    a.K = 1;
+    a.H = cfg->hidden;
+    a.y = m;
+    a.y_bf16 = m_dtype == BEAM_BF16;
+    a.pair_row = nullptr;   // row t of m, weight 1
+    a.w = nullptr;
+    a.h = h;
+    a.x_next = x_next;
+    a.act_bf16 = act_dtype == BEAM_BF16;
+    a.gpost = gamma_post;
+    a.gpre = gamma_pre;
+    a.c_res = (float)sqrt((double)(n - 1) / (double)n);
+    a.c_new = (float)(1.0 / sqrt((double)n));
+    a.eps = cfg->rms_eps;
+    a.moe_out = nullptr;
     return beam::launch_combine_norm(a, static_cast<hipStream_t>(stream)) == hipSuccess ? BEAM_OK
                                                                                          : BEAM_ERR_HIP;
 }

@@ -52,23 +52,27 @@ __global__ __launch_bounds__(256) void beam_combine_norm(CombineArgs a) {
     const int t = blockIdx.x, tid = threadIdx.x;
     const int H = a.H, K = a.K;
     const int TK = a.T * K;
-    const int32_t* prow = a.pair_row + (size_t)t * K;
-    const float* wrow = a.w + (size_t)t * K;
+    // without pair_row the input row is the token's own row with weight 1
+    // (norm boundary on a given m: a dense layer's MLP output or the sum of
+    // expert-parallel partials)
+    const int32_t* prow = a.pair_row ? a.pair_row + (size_t)t * K : nullptr;
+    const float* wrow = a.w ? a.w + (size_t)t * K : nullptr;
 
     float4 m[NIT];
 #pragma unroll
     for (int it = 0; it < NIT; ++it) m[it] = make_float4(0.f, 0.f, 0.f, 0.f);
-    // K expert rows, 8 at a time: indices and weights first, then every
-    // row load of the group in flight together
+    // K expert rows, kRowGroup at a time: indices and weights first, then
+    // every row load of the group in flight together; dropped pairs
+    // (pair_row -1) and anything outside y are skipped
     for (int k0 = 0; k0 < K; k0 += kRowGroup) {
         int rr[kRowGroup];
         float wk[kRowGroup];
 #pragma unroll
         for (int j = 0; j < kRowGroup; ++j) {
             const int k = k0 + j;
-            const int r = k < K ? prow[k] : -1;
+            const int r = k < K ? (prow ? prow[k] : t) : -1;
             rr[j] = ((unsigned)r < (unsigned)TK) ? r : -1;   // never read outside y
-            wk[j] = k < K ? wrow[k] : 0.f;
+            wk[j] = k < K ? (wrow ? wrow[k] : 1.0f) : 0.f;
         }
         float4 yv[kRowGroup][NIT];
 #pragma unroll
@@ -83,6 +87,16 @@ __global__ __launch_bounds__(256) void beam_combine_norm(CombineArgs a) {
         for (int j = 0; j < kRowGroup; ++j)
 #pragma unroll
             for (int it = 0; it < NIT; ++it) m[it] = fma4(wk[j], yv[j][it], m[it]);
+    }
+
+    if (a.partial_only) {   // one expert-parallel shard's share of m: no norm
+        const size_t rowo = (size_t)t * H;
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int i = (it * 256 + tid) * 4;
+            if (i < H) *reinterpret_cast<float4*>(a.moe_out + rowo + i) = m[it];
+        }
+        return;
     }
 
     // post-norm

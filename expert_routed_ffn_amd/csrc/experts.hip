@@ -122,6 +122,8 @@ struct GemmParams {
     const float* wscale;       // fp8: per output row
     const uint8_t* mx_act;     // MXFP4: E8M0 codes of the activation rows [rows, K/32]
     const uint8_t* mx_w;       // MXFP4: E8M0 codes of the weight rows [E, rows, K/32]
+    int ksplit;                // GEMM2 on the direct kernel: K slices (gridDim.y)
+    size_t out_slice;          // elements between the fp32 outputs of two slices
     int H, F;
     void* out;
     bool out_bf16;             // G2 only
@@ -223,7 +225,10 @@ template <int KIND, bool G1>
 BEAM_DEV void gemm_item_direct(const GemmParams& p, int e, int row0, int rows, int tile) {
     const int lane = threadIdx.x & 63;
     const int r = lane & 15, g = lane >> 4;
-    const int kbytes = row_bytes<KIND>(G1 ? p.H : p.F);
+    const int krow = row_bytes<KIND>(G1 ? p.H : p.F);
+    // K slice of this workgroup (the whole row unless GEMM2 is split)
+    const int kslice = krow / p.ksplit;
+    const int kbeg = (int)blockIdx.y * kslice, kbytes = kbeg + kslice;
     int a0, a1;
     const uint8_t *pa0, *pa1;
     weight_rows<KIND, G1>(p, e, tile, a0, a1, pa0, pa1);
@@ -233,10 +238,10 @@ BEAM_DEV void gemm_item_direct(const GemmParams& p, int e, int row0, int rows, i
     const uint8_t* pb;
     if constexpr (G1) {
         tok = bval ? p.row_token[row0 + r] : 0;
-        pb = p.act + (size_t)tok * kbytes + 16 * g;
+        pb = p.act + (size_t)tok * krow + 16 * g;
     } else {
         tok = row0 + r;
-        pb = p.act + (size_t)(bval ? row0 + r : row0) * kbytes + 16 * g;
+        pb = p.act + (size_t)(bval ? row0 + r : row0) * krow + 16 * g;
     }
 
     // MXFP4: E8M0 rows of the lane's two weight rows and its activation row;
@@ -278,15 +283,24 @@ BEAM_DEV void gemm_item_direct(const GemmParams& p, int e, int row0, int rows, i
         }
     };
 
-    load(0, 0);
-    for (int k = 0; k < kbytes; k += 2 * kKIterBytes) {
+    load(0, kbeg);
+    for (int k = kbeg; k < kbytes; k += 2 * kKIterBytes) {
         const bool has1 = k + kKIterBytes < kbytes;
         if (has1) load(1, k + kKIterBytes);
         compute(0);
         if (k + 2 * kKIterBytes < kbytes) load(0, k + 2 * kKIterBytes);
         if (has1) compute(1);
     }
-    if (bval) store_block<KIND, G1>(p, e, a0, a1, (size_t)row0 + r, tok, acc0, acc1);
+    if (!bval) return;
+    if constexpr (!G1) {
+        if (p.ksplit > 1) {   // partial sums of this K slice to its own fp32 output
+            GemmParams q = p;
+            q.out = static_cast<float*>(p.out) + blockIdx.y * p.out_slice;
+            store_block<KIND, G1>(q, e, a0, a1, (size_t)row0 + r, tok, acc0, acc1);
+            return;
+        }
+    }
+    store_block<KIND, G1>(p, e, a0, a1, (size_t)row0 + r, tok, acc0, acc1);
 }
 
 // ---- large items (<= kLdsRows rows): the item's activation rows are staged
@@ -794,8 +808,8 @@ static void launch_gemm(GemmParams p, int n_items_max, GemmPath path, hipStream_
     }
     p.n_tiles = G1 ? F / 64 : H / 128;
     if (path == PATH_DIRECT)
-        hipLaunchKernelGGL((beam_expert_gemm_direct<KIND, G1>), dim3(n_items_max * p.n_tiles), dim3(256), 0,
-                           st, p);
+        hipLaunchKernelGGL((beam_expert_gemm_direct<KIND, G1>), dim3(n_items_max * p.n_tiles, G1 ? 1 : p.ksplit),
+                           dim3(256), 0, st, p);
     else
         hipLaunchKernelGGL((beam_expert_gemm_lds<KIND, G1>), dim3(n_items_max * p.n_tiles), dim3(256), 0, st, p);
 }
@@ -821,6 +835,7 @@ hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st) {
     p.n_items = ws.n_items;
     p.H = a.H;
     p.F = a.F;
+    p.ksplit = 1;
 
     // GEMM1 + SwiGLU
     p.act = static_cast<const uint8_t*>(a.x);
@@ -842,7 +857,11 @@ hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st) {
         launch_gemm<W_FP8, true>(p, n_items_max, path, st);
     }
 
-    // GEMM2
+    // GEMM2 (split over K on the direct kernel when the caller asks)
+    if (path == PATH_DIRECT && a.ksplit > 1) {
+        p.ksplit = a.ksplit;
+        p.out_slice = a.y_slice_stride;
+    }
     p.row_token = nullptr;
     p.W = static_cast<const uint8_t*>(a.wd);
     p.wscale = static_cast<const float*>(a.sd);
@@ -868,6 +887,41 @@ hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st) {
         p.act_scale = nullptr;
         launch_gemm<W_BF16, false>(p, n_items_max, path, st);
     }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- dense layer helpers
+
+__global__ __launch_bounds__(256) void beam_sum_slices(const float* __restrict__ parts, int S, size_t n,
+                                                       float* __restrict__ y) {
+    const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= n) return;                              // n % 4 == 0
+    float4 acc = *reinterpret_cast<const float4*>(parts + i);
+    for (int s = 1; s < S; ++s) {                    // fixed order: deterministic
+        const float4 v = *reinterpret_cast<const float4*>(parts + (size_t)s * n + i);
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    *reinterpret_cast<float4*>(y + i) = acc;
+}
+
+__global__ __launch_bounds__(256) void beam_dense_rows(int T, int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ row_token) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < T) row_token[i] = i;
+    if (i == 0) {
+        offsets[0] = 0;
+        offsets[1] = T;
+    }
+}
+
+hipError_t launch_sum_slices(const float* parts, int S, size_t n, float* y, hipStream_t st) {
+    const size_t blocks = (n / 4 + 255) / 256;
+    hipLaunchKernelGGL(beam_sum_slices, dim3((unsigned)blocks), dim3(256), 0, st, parts, S, n, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_dense_rows(int T, int32_t* offsets, int32_t* row_token, hipStream_t st) {
+    hipLaunchKernelGGL(beam_dense_rows, dim3((T + 255) / 256), dim3(256), 0, st, T, offsets, row_token);
     return hipGetLastError();
 }
 

@@ -26,6 +26,7 @@ size_t route_partials_bytes(int T, int H, int E);
 
 struct PermuteArgs {
     int T, K, E, H;
+    int e_base;             // ids are taken relative to it; ids outside [e_base, e_base + E) are dropped
     const int32_t* ids;
     int32_t* offsets;
     int32_t* row_token;
@@ -54,9 +55,18 @@ struct ExpertsArgs {
     void* y;
     bool y_bf16;
     void* ws;
+    // split of the down projection's K over gridDim.y slices (direct kernel
+    // only); slice s writes its partial sums to y + s * y_slice_stride
+    int ksplit = 1;
+    size_t y_slice_stride = 0;
 };
 size_t experts_ws_bytes(int T, int K, int E, int H, int F, WKind w);
 hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st);
+
+// y[i] = sum over s of parts[s * n + i], s = 0..S-1 in order
+hipError_t launch_sum_slices(const float* parts, int S, size_t n, float* y, hipStream_t st);
+// offsets = {0, T}, row_token = 0..T-1 (the dense MLP as one expert over all rows)
+hipError_t launch_dense_rows(int T, int32_t* offsets, int32_t* row_token, hipStream_t st);
 
 // Reorders `rows` rows of `kb` bytes (rows % 16 == 0, kb % 256 == 0) into
 // the packed tile layout of the expert GEMM.
@@ -81,6 +91,7 @@ struct CombineArgs {
     const void* gpre;
     float c_res, c_new, eps;
     float* moe_out;
+    bool partial_only;      // write m to moe_out and stop (no norm boundary)
 };
 hipError_t launch_combine_norm(const CombineArgs& a, hipStream_t st);
 

@@ -19,7 +19,7 @@ constexpr int kMaxE = 256;
 // are taken 256 at a time; inside a wave the rank among equal experts comes
 // from ballots over the expert id bits, and the four waves of a chunk
 // claim their rows one after another so the order of p is kept.
-BEAM_DEV void stable_scatter(const int32_t* __restrict__ ids, int begin, int end, int K,
+BEAM_DEV void stable_scatter(const int32_t* __restrict__ ids, int e_base, int begin, int end, int K,
                              int E, int ebits, int* cursor, int32_t* __restrict__ row_token,
                              int32_t* __restrict__ pair_row) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -27,7 +27,7 @@ BEAM_DEV void stable_scatter(const int32_t* __restrict__ ids, int begin, int end
     for (int base = begin; base < end; base += kPermThreads) {
         const int p = base + threadIdx.x;
         bool valid = p < end;
-        int e = valid ? ids[p] : 0;
+        int e = valid ? ids[p] - e_base : 0;
         if (valid && (unsigned)e >= (unsigned)E) {   // out-of-range ids are dropped
             pair_row[p] = -1;
             valid = false;
@@ -55,7 +55,7 @@ BEAM_DEV void stable_scatter(const int32_t* __restrict__ ids, int begin, int end
 
 // Whole permutation in one workgroup (T*K <= kPermChunk).
 __global__ __launch_bounds__(kPermThreads) void beam_permute_fused(
-    const int32_t* __restrict__ ids, int TK, int K, int E, int ebits,
+    const int32_t* __restrict__ ids, int e_base, int TK, int K, int E, int ebits,
     int32_t* __restrict__ offsets, int32_t* __restrict__ row_token, int32_t* __restrict__ pair_row) {
     __shared__ int hist[kMaxE];
     __shared__ int cursor[kMaxE];
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kPermThreads) void beam_permute_fused(
     if (tid < E) hist[tid] = 0;
     __syncthreads();
     for (int p = tid; p < TK; p += kPermThreads) {
-        const int e = ids[p];
+        const int e = ids[p] - e_base;
         if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);
     }
     __syncthreads();
@@ -76,12 +76,12 @@ __global__ __launch_bounds__(kPermThreads) void beam_permute_fused(
     }
     if (tid == 0) offsets[E] = total;
     __syncthreads();
-    stable_scatter(ids, 0, TK, K, E, ebits, cursor, row_token, pair_row);
+    stable_scatter(ids, e_base, 0, TK, K, E, ebits, cursor, row_token, pair_row);
 }
 
 // Multi-block path, step 1: per-chunk histograms bh[b][e].
 __global__ __launch_bounds__(kPermThreads) void beam_permute_hist(
-    const int32_t* __restrict__ ids, int TK, int E, int32_t* __restrict__ bh) {
+    const int32_t* __restrict__ ids, int e_base, int TK, int E, int32_t* __restrict__ bh) {
     __shared__ int hist[kMaxE];
     const int tid = threadIdx.x;
     if (tid < E) hist[tid] = 0;
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(kPermThreads) void beam_permute_hist(
     const int begin = blockIdx.x * kPermChunk;
     const int end = min(begin + kPermChunk, TK);
     for (int p = begin + tid; p < end; p += kPermThreads) {
-        const int e = ids[p];
+        const int e = ids[p] - e_base;
         if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);
     }
     __syncthreads();
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(kPermThreads) void beam_permute_scan(
 
 // Step 3: stable scatter of each chunk from its per-expert base rows.
 __global__ __launch_bounds__(kPermThreads) void beam_permute_scatter(
-    const int32_t* __restrict__ ids, int TK, int K, int E, int ebits,
+    const int32_t* __restrict__ ids, int e_base, int TK, int K, int E, int ebits,
     const int32_t* __restrict__ bbase, int32_t* __restrict__ row_token,
     int32_t* __restrict__ pair_row) {
     __shared__ int cursor[kMaxE];
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(kPermThreads) void beam_permute_scatter(
     __syncthreads();
     const int begin = blockIdx.x * kPermChunk;
     const int end = min(begin + kPermChunk, TK);
-    stable_scatter(ids, begin, end, K, E, ebits, cursor, row_token, pair_row);
+    stable_scatter(ids, e_base, begin, end, K, E, ebits, cursor, row_token, pair_row);
 }
 
 // Dynamic per-token e4m3 quantisation of x: one workgroup per token row.
@@ -159,15 +159,15 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t st) {
     while ((1 << ebits) < a.E) ++ebits;
     const int nb = n_chunks(TK);
     if (nb <= 1) {
-        hipLaunchKernelGGL(beam_permute_fused, dim3(1), dim3(kPermThreads), 0, st, a.ids, TK, a.K,
+        hipLaunchKernelGGL(beam_permute_fused, dim3(1), dim3(kPermThreads), 0, st, a.ids, a.e_base, TK, a.K,
                            a.E, ebits, a.offsets, a.row_token, a.pair_row);
     } else {
         int32_t* bh = static_cast<int32_t*>(a.ws);
         int32_t* bb = bh + (size_t)nb * a.E;
-        hipLaunchKernelGGL(beam_permute_hist, dim3(nb), dim3(kPermThreads), 0, st, a.ids, TK, a.E, bh);
+        hipLaunchKernelGGL(beam_permute_hist, dim3(nb), dim3(kPermThreads), 0, st, a.ids, a.e_base, TK, a.E, bh);
         hipLaunchKernelGGL(beam_permute_scan, dim3(1), dim3(kPermThreads), 0, st, bh, nb, TK, a.E,
                            a.offsets, bb);
-        hipLaunchKernelGGL(beam_permute_scatter, dim3(nb), dim3(kPermThreads), 0, st, a.ids, TK, a.K,
+        hipLaunchKernelGGL(beam_permute_scatter, dim3(nb), dim3(kPermThreads), 0, st, a.ids, a.e_base, TK, a.K,
                            a.E, ebits, bb, a.row_token, a.pair_row);
     }
     hipError_t err = hipGetLastError();

@@ -253,6 +253,78 @@ beam_status beam_moe_combine_norm(const beam_moe_cfg* cfg, int32_t T,
                                   int32_t n, float* moe_out, void* stream);
 
 /*
+ * beam_moe_norm_boundary -- the sandwich-norm boundary on a given m: the
+ * same post-RMSNorm, depth-scaled residual and next pre-RMSNorm as
+ * beam_moe_combine_norm, with m supplied by the caller instead of combined
+ * from expert rows.  For a dense layer's MLP output, and for the sum of the
+ * expert-parallel shards' partial outputs after the all-reduce.
+ * (TokenSpeed blog, "Architecture": a norm before and after every block;
+ *  "Tensor parallelism and expert parallelism": under EP8 the
+ *  normalisation runs separately from the all-reduce.)
+ *   m      [T,H] F32 or BF16 (m_dtype); h, x_next, gammas, n as in
+ *          beam_moe_combine_norm (h updated in place, must not alias x_next)
+ */
+beam_status beam_moe_norm_boundary(const beam_moe_cfg* cfg, int32_t T, const void* m, beam_dtype m_dtype,
+                                   void* h, void* x_next, beam_dtype act_dtype,
+                                   const void* gamma_post, const void* gamma_pre, int32_t n, void* stream);
+
+/*
+ * beam_moe_permute_shard -- beam_moe_permute restricted to one
+ * expert-parallel shard: the pairs whose expert lies in
+ * [expert_begin, expert_begin + n_local) are grouped by local expert
+ * (id - expert_begin) in the same stable order; every other pair gets
+ * pair_row[p] = -1.  (TokenSpeed blog, "Tensor parallelism and expert
+ * parallelism": with EP8 each GPU holds 32 complete experts and processes
+ * the tokens routed to them; Gaudi cookbook, "At a glance": EP 8, 32
+ * experts per card -- exactly one routing group.)
+ *   expert_offsets [n_local+1], row_token [T*K] (the first
+ *   expert_offsets[n_local] entries used), pair_row [T*K]
+ *   ws              required when T*K > 4096, 16-byte aligned; at most the
+ *                   size beam_moe_workspace_bytes gives for the full layer
+ * The shard's experts then run through beam_moe_experts with a cfg whose
+ * n_experts is n_local and the shard's slices of the weight stacks.
+ */
+beam_status beam_moe_permute_shard(const beam_moe_cfg* cfg, int32_t T, int32_t expert_begin, int32_t n_local,
+                                   const int32_t* topk_ids, int32_t* expert_offsets, int32_t* row_token,
+                                   int32_t* pair_row, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * beam_moe_combine_partial -- one shard's share of the weighted combine:
+ *   m_out[t] = sum over k with pair_row[t*K+k] >= 0 of topk_w[t,k] * y[pair_row[t*K+k]]
+ * (fp32, no norm).  The shards' m_out summed over all shards (the
+ * all-reduce) equal the layer's m.  (TokenSpeed blog, "Tensor parallelism
+ * and expert parallelism": the all-reduce sums the MoE output, no
+ * all-to-all.)
+ *   y [T*K,H] F32|BF16, pair_row [T*K] from beam_moe_permute_shard,
+ *   topk_w [T,K], m_out [T,H] fp32 out
+ */
+beam_status beam_moe_combine_partial(const beam_moe_cfg* cfg, int32_t T, const void* y, beam_dtype y_dtype,
+                                     const int32_t* pair_row, const float* topk_w, float* m_out, void* stream);
+
+/*
+ * beam_moe_dense_mlp -- the SwiGLU MLP of a dense layer over all T tokens:
+ *   y[t] = (silu(x[t] W_gu[0:d_ff]^T) * x[t] W_gu[d_ff:2 d_ff]^T) W_down^T
+ * with the SwiGLU output rounded to bf16, fp32 accumulation, y fp32 (the
+ * expert GEMMs with one "expert" holding every row).  (vLLM Beam summary,
+ * MoE section: layers 0-2 use a dense SwiGLU MLP with d_ff 20480 instead of
+ * the MoE; TokenSpeed blog, "Architecture": the first 3 layers are dense.)
+ *   d_ff      multiple of 128, at most 32768 (cfg->d_ff is not used)
+ *   x         [T,H] BF16
+ *   w_gate_up [2 d_ff, H] bf16, w_down [H, d_ff] bf16, both packed by
+ *             beam_moe_pack_weights (a cfg with this d_ff, n_experts 1)
+ *   y         [T,H] fp32 out
+ *   ws        beam_moe_dense_workspace_bytes(cfg, T, d_ff) bytes, 16-byte
+ *             aligned; at T <= 16 the down projection is split over K and
+ *             its slices are summed in a fixed order (deterministic)
+ */
+beam_status beam_moe_dense_mlp(const beam_moe_cfg* cfg, int32_t T, int32_t d_ff, const void* x,
+                               beam_dtype x_dtype, const void* w_gate_up, const void* w_down, float* y,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes of beam_moe_dense_mlp for T tokens (0 for invalid input). */
+size_t beam_moe_dense_workspace_bytes(const beam_moe_cfg* cfg, int32_t T, int32_t d_ff);
+
+/*
  * beam_moe_pack_weights -- one-time re-layout of expert weight stacks into
  * the tiled order beam_moe_experts streams from (load time, not per layer
  * call).  Each expert matrix of R rows x KB bytes is cut into 16-row x
@@ -262,7 +334,8 @@ beam_status beam_moe_combine_norm(const beam_moe_cfg* cfg, int32_t T,
  * packed layout is the plain row-major one (a copy).
  *
  *   n_experts       number of expert matrices in each stack (may be a
- *                   subset of cfg->n_experts, to pack expert by expert)
+ *                   subset of cfg->n_experts, to pack expert by expert);
+ *                   cfg->d_ff may be up to 32768 here (the dense layers)
  *   w_gate_up       [n_experts,2F,H] row-major in; w_down [n_experts,H,F]
  *                   (MXFP4: the packed E2M1 bytes, K/2 per row; the E8M0
  *                   scales are not re-laid out)

@@ -178,3 +178,35 @@ def test_experts_static_checks(L):
     # rejected before anything is enqueued
     assert L.beam_moe_workspace_bytes(ctypes.byref(c), 4096, 1) > beam.STATIC_SCRATCH_BYTES
     assert f(T=4096) == 2
+
+
+def test_shard_dense_norm_checks(L):
+    c = _cfg()
+    # permute_shard: the expert range must lie inside the layer's experts
+    ps = lambda eb=0, n=32, T=8: L.beam_moe_permute_shard(ctypes.byref(c), T, eb, n, FAKE, FAKE, FAKE, FAKE,
+                                                         None, 0, None)
+    assert ps(eb=-1) == 1
+    assert ps(eb=240, n=32) == 1
+    assert ps(n=0) == 1
+    assert ps(T=0) == 0
+    assert ps(T=4096) == 3                     # multi-block permutation needs workspace
+    # combine_partial: fp32 output required, y dtype checked
+    cp = lambda y_dt=0, m=FAKE: L.beam_moe_combine_partial(ctypes.byref(c), 8, FAKE, y_dt, FAKE, FAKE, m, None)
+    assert cp(y_dt=2) == 1
+    assert cp(m=None) == 1
+    # norm boundary: residual index >= 1, no aliasing of h and x_next
+    nb = lambda n=20, h=FAKE, xn=FAKE + 4096: L.beam_moe_norm_boundary(ctypes.byref(c), 8, FAKE, 0, h, xn, 1,
+                                                                       FAKE, FAKE, n, None)
+    assert nb(n=0) == 1
+    assert nb(xn=FAKE) == 1
+    # dense MLP: d_ff a multiple of 128 and at most 32768, bf16 input, workspace
+    dm = lambda d_ff=20480, x_dt=1, ws=FAKE, wsb=1 << 40: L.beam_moe_dense_mlp(
+        ctypes.byref(c), 8, d_ff, FAKE, x_dt, FAKE, FAKE, FAKE, ws, wsb, None)
+    assert dm(d_ff=20000) == 2
+    assert dm(d_ff=65536) == 2
+    assert dm(x_dt=0) == 1
+    assert dm(ws=None) == 3
+    assert dm(wsb=1024) == 3
+    assert L.beam_moe_dense_workspace_bytes(ctypes.byref(c), 8, 20480) > \
+        L.beam_moe_dense_workspace_bytes(ctypes.byref(c), 8, 2560) > 0
+    assert L.beam_moe_dense_workspace_bytes(ctypes.byref(c), 8, 100) == 0
