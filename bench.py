@@ -7,8 +7,10 @@ and all 256 experts' weights resident in HBM.  The headline line is the
 Beam decode shape (T = 8 tokens, bf16 experts); the same JSON line carries
 the other shapes the metric is quoted on (T = 64 with skewed routes,
 T = 2048 prefill, T = 16384 with fp8 experts, and T = 16384 with bf16
-experts) and the decode shapes with 4-bit MXFP4 experts (T = 8 and 64)
-under "configs".  Prints one JSON line.
+experts), the decode shapes with 4-bit MXFP4 experts (T = 8 and 64), the
+dense layers (d_ff 20480, T = 8 and 2048) and one GPU's share of the layer
+under 8-way expert parallelism (T = 8 and 2048) under "configs".  Prints
+one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--configs a,b|none]
 
@@ -43,7 +45,7 @@ RIDGE_ROWS = 312.5               # rows per expert where weight streaming stops 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 EXPERTS_SRC = os.path.join(ROOT, "expert_routed_ffn_amd", "csrc", "experts.hip")
 DEFAULT_CONFIGS = ("skew_t64,prefill_t2048,prefill_fp8_t16384,prefill_bf16_t16384,"
-                   "decode_t8_mxfp4,skew_t64_mxfp4")
+                   "decode_t8_mxfp4,skew_t64_mxfp4,dense_t8,dense_t2048,ep8_shard_t8,ep8_shard_t2048")
 METRIC = "MoE-layer tokens/s (one Beam MoE layer forward incl. routing and norm boundary)"
 
 
@@ -316,6 +318,128 @@ def cpu_baseline(wl, state, n_tokens, min_seconds=10.0, max_reps=8):
                       f"{reps} passes, {dt:.1f} s on {cores} host threads"}
 
 
+def time_dense(wl, steps, warmup, hipev, dev):
+    """Dense layer step: beam_moe_dense_mlp + beam_moe_norm_boundary."""
+    import torch
+    import expert_routed_ffn_amd as beam
+    import synth
+    cfg = lcfg(wl)
+    w_gu, w_d, _, _ = synth.make_expert(wl, 0, dev)
+    pgu, pd = torch.empty_like(w_gu), torch.empty_like(w_d)
+    beam.beam_moe_pack_weights(cfg, w_gu.unsqueeze(0), w_d.unsqueeze(0), pgu.unsqueeze(0), pd.unsqueeze(0))
+    del w_gu, w_d
+    x, h, gp, gq = synth.make_activations(wl, dev)
+    y = torch.empty((wl.T, wl.hidden), dtype=torch.float32, device=dev)
+    xn = torch.empty_like(h)
+    ws = beam.dense_workspace(cfg, wl.T, wl.d_ff)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step(evs=None):
+        if evs:
+            hipev.record(evs[0], stream)
+        beam.beam_moe_dense_mlp(cfg, x, pgu, pd, y, ws)
+        if evs:
+            hipev.record(evs[1], stream)
+        beam.beam_moe_norm_boundary(cfg, y, h, xn, gp, gq, wl.n)
+        if evs:
+            hipev.record(evs[2], stream)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[hipev.create() for _ in range(3)] for _ in range(steps)]
+    t0, t1 = hipev.create(), hipev.create()
+    hipev.record(t0, stream)
+    for i in range(steps):
+        step(evs[i])
+    hipev.record(t1, stream)
+    torch.cuda.synchronize()
+    mlp = [hipev.elapsed_ms(e[0], e[1]) * 1e3 for e in evs]
+    nb = [hipev.elapsed_ms(e[1], e[2]) * 1e3 for e in evs]
+    layer = [hipev.elapsed_ms(e[0], e[2]) * 1e3 for e in evs]
+    us = hipev.elapsed_ms(t0, t1) * 1e3 / steps
+    H, Fd, T = wl.hidden, wl.d_ff, wl.T
+    mlp_us = sum(mlp) / len(mlp)
+    wbytes = 3 * H * Fd * 2 + T * H * 2
+    flops = 6 * H * Fd * T
+    if T >= RIDGE_ROWS:
+        ach = flops / (mlp_us / 1e6) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / BF16_MFMA_TFLOPS, 4), "algorithmic_flops": flops}
+    else:
+        ach = wbytes / (mlp_us / 1e6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "algorithmic_bytes": wbytes}
+    roof.update({"kernel": "beam_moe_dense_mlp call (GEMM1 + SwiGLU, GEMM2" +
+                 (", K-slice sum" if T <= 16 else "") + ")", "kernel_avg_us": round(mlp_us, 2)})
+    return {"us_per_layer": round(us, 1), "tokens_per_s": round(T / (us / 1e6), 1), "T": T, "d_ff": Fd,
+            "expert_weights": "bf16 (dense)", "layer_us": stats(layer),
+            "stages_us_median": {"dense_mlp": round(statistics.median(mlp), 2),
+                                 "norm_boundary": round(statistics.median(nb), 2)},
+            "roofline": roof}
+
+
+def time_ep_shards(wl, stacks, steps, warmup, hipev, dev, n_shards=8):
+    """One GPU's share of the layer under EP8, for each of the 8 groups of 32
+    experts in turn: beam_moe_permute_shard, beam_moe_experts on the group's
+    slice of the stacks, beam_moe_combine_partial (the routes computed once,
+    as every GPU computes the same routes).  The all-reduce and the norm
+    boundary that follows it are not part of a shard."""
+    import torch
+    import expert_routed_ffn_amd as beam
+    s = layer_setup(wl, stacks, dev)
+    run_step(wl, s)                       # routes and the unsharded layer
+    torch.cuda.synchronize()
+    cfg, b = s["cfg"], s["bufs"]
+    per = wl.n_experts // n_shards
+    scfg = beam.LayerCfg(wl.hidden, per, 1, 1, wl.topk, wl.group_topn, wl.d_ff, wl.routed_scale, wl.rms_eps)
+    T, K, H = wl.T, wl.topk, wl.hidden
+    off = torch.empty(per + 1, dtype=torch.int32, device=dev)
+    rt = torch.empty(T * K, dtype=torch.int32, device=dev)
+    pr = torch.empty(T * K, dtype=torch.int32, device=dev)
+    m = torch.empty((T, H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    shards = []
+    for r in range(n_shards):
+        eb = r * per
+        wg, wdn = s["wgu"][eb:eb + per], s["wd"][eb:eb + per]
+
+        def step(evs=None):
+            if evs:
+                hipev.record(evs[0], stream)
+            beam.beam_moe_permute_shard(cfg, b.topk_ids, eb, per, off, rt, pr, ws=b.ws)
+            if evs:
+                hipev.record(evs[1], stream)
+            beam.beam_moe_experts(scfg, T, s["x"], off, rt, wg, wdn, b.y, ws=b.ws)
+            if evs:
+                hipev.record(evs[2], stream)
+            beam.beam_moe_combine_partial(cfg, b.y, pr, b.topk_w, m)
+            if evs:
+                hipev.record(evs[3], stream)
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        evs = [[hipev.create() for _ in range(4)] for _ in range(steps)]
+        for i in range(steps):
+            step(evs[i])
+        torch.cuda.synchronize()
+        tot = sum(hipev.elapsed_ms(e[0], e[3]) for e in evs) * 1e3 / steps
+        ex = sum(hipev.elapsed_ms(e[1], e[2]) for e in evs) * 1e3 / steps
+        D = int(((off[1:] - off[:-1]) > 0).sum())
+        alg = D * 3 * H * wl.d_ff * 2 + T * H * 2
+        shards.append({"shard": r, "us": round(tot, 1), "experts_us": round(ex, 1), "experts_touched": D,
+                       "experts_hbm_frac": round(alg / (ex / 1e6) / 1e9 / HBM_PEAK_GBS, 4)})
+    worst = max(shards, key=lambda d: d["us"])
+    ach = worst["experts_touched"] * 3 * H * wl.d_ff * 2 + T * H * 2
+    return {"T": T, "shards": n_shards, "experts_per_shard": per,
+            "shard_us_max": worst["us"], "shard_us_mean": round(sum(d["us"] for d in shards) / n_shards, 1),
+            "roofline": {"bound": "hbm", "achieved": round(ach / (worst["experts_us"] / 1e6) / 1e9, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": worst["experts_hbm_frac"], "algorithmic_bytes": ach,
+                         "kernel": f"beam_moe_experts call of the slowest shard ({worst['shard']})",
+                         "kernel_avg_us": worst["experts_us"]},
+            "per_shard": shards}
+
+
 def entry(wl, r):
     roof, layer = roofline_entry(wl, r)
     sec = r["ms_per_step"] / 1e3
@@ -395,7 +519,20 @@ def main():
     names = [] if args.configs == "none" else [n for n in args.configs.split(",") if n and n != wl.name]
     cfgs = {}
     for name in names:
+        if name.startswith("ep8_shard_"):
+            base = {"ep8_shard_t8": "decode_t8", "ep8_shard_t2048": "prefill_t2048"}[name]
+            w2 = synth.WORKLOADS[base]
+            if w2.w_dtype not in by_dtype:
+                by_dtype[w2.w_dtype] = packed_stacks(w2, dev)
+            cfgs[name] = time_ep_shards(w2, by_dtype[w2.w_dtype], args.steps, min(args.warmup, 3), hipev, dev)
+            print(f"# {name}: slowest shard {cfgs[name]['shard_us_max']} us", file=sys.stderr, flush=True)
+            continue
         w2 = synth.WORKLOADS[name]
+        if w2.dense:
+            cfgs[name] = time_dense(w2, args.steps, min(args.warmup, 3), hipev, dev)
+            print(f"# {name}: {cfgs[name]['us_per_layer']} us/layer", file=sys.stderr, flush=True)
+            torch.cuda.empty_cache()
+            continue
         if w2.w_dtype not in by_dtype:
             by_dtype[w2.w_dtype] = packed_stacks(w2, dev)
         r2 = time_workload(w2, by_dtype[w2.w_dtype], args.steps, min(args.warmup, 3), hipev, dev,
