@@ -307,6 +307,8 @@ BEAM_DEV void gemm_item_direct(const GemmParams& p, int e, int row0, int rows, i
 // once per workgroup in LDS (double-buffered, 256 bytes of K per stage) and
 // shared by the 4 waves; weights keep streaming into registers.
 constexpr int kLdsRows = 128;
+constexpr int kWideRows = 128;   // rows of a work item on the wide path
+constexpr int kLook = 3;         // wide path: LDS fragment reads issued this many groups ahead
 
 // LDS position of 16-byte chunk c of staged row rr: chunks are XOR-swizzled
 // with the row's low 4 bits so the 16 rows read by one MFMA fragment load
@@ -512,7 +514,7 @@ BEAM_DEV i32x8 pair8(uint4 lo, uint4 hi) {
 
 template <int KIND, bool G1, int NB, bool NT>
 BEAM_DEV void gemm_item_wide(const GemmParams& p, int e, int row0, int rows, int tile,
-                             uint4 (*bs)[kLdsRows * 16]) {
+                             uint4 (*bs)[kWideRows * 16]) {
     constexpr int NS = (KIND == W_BF16) ? 4 : 2;   // MFMA steps per 256-byte K iteration
     const int lane = threadIdx.x & 63;
     const int r = lane & 15, g = lane >> 4;
@@ -565,49 +567,73 @@ BEAM_DEV void gemm_item_wide(const GemmParams& p, int e, int row0, int rows, int
             else wa[j][st] = pair8(wload(j, 2 * st, k), wload(j, 2 * st + 1, k));
         }
     };
+    // B fragment q of a K iteration (q = st * NB + nb): the 16 rows of row
+    // block nb for MFMA step st, from the staged LDS tile
+    auto bload = [&](const uint4* b, int q) -> WFrag {
+        const int st = q / NB, nb = q % NB;
+        if constexpr (KIND == W_BF16) return b[lds_pos(nb * 16 + r, 4 * st + g)];
+        else return pair8(b[lds_pos(nb * 16 + r, 4 * (2 * st) + g)], b[lds_pos(nb * 16 + r, 4 * (2 * st + 1) + g)]);
+    };
     gload(0);
 #pragma unroll
     for (int st = 0; st < NS; ++st) aload_step(st, 0);
     swrite(0);
     __syncthreads();
-    // One straight-line body for both LDS buffers (runtime buffer index):
-    // the weight registers are reloaded in place, and with no branches in
-    // the body the scheduling barriers keep every MFMA step ahead of the
-    // reload of its own weight registers.  The last iteration reloads its
-    // own K slice (in bounds, never used).
-    for (int kit = 0; kit < nk; ++kit) {
-        const int cur = kit & 1;
+    // One straight-line body per LDS buffer, the pair unrolled in the loop
+    // (no runtime buffer index).  The NS * NB fragment groups of an iteration run
+    // as one sequence with the LDS reads kLook groups ahead of their MFMAs
+    // (one wave per SIMD: nothing else hides the LDS latency), and the
+    // weight registers of step st are reloaded right after the step's last
+    // MFMA; with no branches in the body the scheduling barriers keep that
+    // order.  The last iteration reloads its own K slice (in bounds, never
+    // used).
+    constexpr int NQ = NS * NB;
+    constexpr int kReadsPerFrag = KIND == W_BF16 ? 1 : 2;   // 16-byte LDS reads per B fragment
+    // instruction classes of the scheduling-group hints
+    constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
+    constexpr int LOOK = kLook < NQ ? kLook : NQ;
+    auto body = [&](auto curc, int kit) {
+        constexpr int cur = decltype(curc)::value;
         const int knext = (kit + 1 < nk ? kit + 1 : kit) * kKIterBytes;
         gload(knext);
         const uint4* bcur = bs[cur];
+        WFrag xq[LOOK];
 #pragma unroll
-        for (int st = 0; st < NS; ++st) {
+        for (int d = 0; d < LOOK; ++d) xq[d] = bload(bcur, d);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, LOOK * kReadsPerFrag, 0);
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                if constexpr (KIND == W_BF16) {
-                    const uint4 xb = bcur[lds_pos(nb * 16 + r, 4 * st + g)];
+        for (int q = 0; q < NQ; ++q) {
+            const int st = q / NB, nb = q % NB;
+            const WFrag xb = xq[q % LOOK];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc[j][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, wa[j][st]), __builtin_bit_cast(bf16x8, xb), acc[j][nb],
-                            0, 0, 0);
-                } else {
-                    const i32x8 bv = pair8(bcur[lds_pos(nb * 16 + r, 4 * (2 * st) + g)],
-                                           bcur[lds_pos(nb * 16 + r, 4 * (2 * st + 1) + g)]);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        // formats 0/0 = e4m3 x e4m3; block scales 127 = 2^0 (unscaled)
-                        acc[j][nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa[j][st], bv, acc[j][nb],
-                                                                                      0, 0, 0, 127, 0, 127);
-                }
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (KIND == W_BF16)
+                    acc[j][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, wa[j][st]), __builtin_bit_cast(bf16x8, xb), acc[j][nb], 0, 0, 0);
+                else   // formats 0/0 = e4m3 x e4m3; block scales 127 = 2^0 (unscaled)
+                    acc[j][nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa[j][st], xb, acc[j][nb],
+                                                                                  0, 0, 0, 127, 0, 127);
             }
-            __builtin_amdgcn_sched_barrier(0);
-            aload_step(st, knext);
-            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
+            if (q + LOOK < NQ) {
+                xq[q % LOOK] = bload(bcur, q + LOOK);
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kReadsPerFrag, 0);
+            }
+            if (nb == NB - 1) {
+                __builtin_amdgcn_sched_barrier(0);
+                aload_step(st, knext);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         swrite(cur ^ 1);
         __syncthreads();
+    };
+    int kit = 0;
+    for (; kit + 1 < nk; kit += 2) {
+        body(IC<0>{}, kit);
+        body(IC<1>{}, kit + 1);
     }
+    if (kit < nk) body(IC<0>{}, kit);   // odd K-iteration count: the last one
 
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -627,10 +653,8 @@ BEAM_DEV void gemm_item_wide(const GemmParams& p, int e, int row0, int rows, int
 }
 
 template <int KIND, bool G1, bool NT>
-BEAM_DEV void dispatch_wide(const GemmParams& p, int4 it, int tile, uint4 (*bs)[kLdsRows * 16]) {
-    if (it.z <= 16)
-        gemm_item_wide<KIND, G1, 1, NT>(p, it.x, it.y, it.z, tile, bs);
-    else if (it.z <= 32)
+BEAM_DEV void dispatch_wide(const GemmParams& p, int4 it, int tile, uint4 (*bs)[kWideRows * 16]) {
+    if (it.z <= 32)
         gemm_item_wide<KIND, G1, 2, NT>(p, it.x, it.y, it.z, tile, bs);
     else if (it.z <= 64)
         gemm_item_wide<KIND, G1, 4, NT>(p, it.x, it.y, it.z, tile, bs);
@@ -646,7 +670,7 @@ BEAM_DEV void dispatch_wide(const GemmParams& p, int4 it, int tile, uint4 (*bs)[
 // all the items of its expert.
 template <int KIND, bool G1>
 __global__ __launch_bounds__(256, 1) void beam_expert_gemm_wide(GemmParams p) {
-    __shared__ uint4 bs[2][kLdsRows * 16];
+    __shared__ uint4 bs[2][kWideRows * 16];
     const int total = *p.n_items * p.n_tiles;
     const int per_xcd = (total + 7) >> 3;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
@@ -729,14 +753,35 @@ __global__ __launch_bounds__(256) void beam_expert_f32_gemm2(
 
 static size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-// Decode-sized batches use 16-row items (every touched expert is one item,
-// so weights are read exactly once); larger batches use 128-row items whose
-// activations are shared through LDS.
-static int rows_per_item(int T) { return T <= 16 ? 16 : kLdsRows; }
+// Kernel choice by the mean rows per expert, T*K/E:
+//   T <= 16:   one 16-row item per touched expert, weights straight into
+//              registers (beam_expert_gemm_direct), so weights are read
+//              exactly once;
+//   < 256:     mostly one 128-row item per expert, so each weight byte is
+//              streamed once: two 16-row weight tiles per wave, two waves
+//              per SIMD for more bytes in flight (beam_expert_gemm_lds);
+//   >= 256:    256-row items, several per expert, sharing each weight tile
+//              through L2: four weight tiles per wave, XCD-grouped work
+//              order (beam_expert_gemm_wide), grid rounded to whole XCD
+//              rounds.
+enum GemmPath { PATH_DIRECT, PATH_LDS, PATH_WIDE };
+
+static GemmPath gemm_path(int T, int K, int E) {
+    if (T <= 16) return PATH_DIRECT;
+    return (long long)T * K >= 256LL * E ? PATH_WIDE : PATH_LDS;
+}
+
+static int rows_per_item(int T, int K, int E) {
+    switch (gemm_path(T, K, E)) {
+        case PATH_DIRECT: return 16;
+        case PATH_LDS: return kLdsRows;
+        default: return kWideRows;
+    }
+}
 
 static size_t max_items(int T, int K, int E) {
     const size_t TK = (size_t)T * K;
-    return TK / rows_per_item(T) + (size_t)std::min<size_t>(E, TK);
+    return TK / rows_per_item(T, K, E) + (size_t)std::min<size_t>(E, TK);
 }
 
 struct ExpertsWs {
@@ -781,21 +826,6 @@ size_t experts_ws_bytes(int T, int K, int E, int H, int F, WKind w) {
     return carve(nullptr, T, K, E, F, w).bytes;
 }
 
-// Kernel choice by the mean rows per expert, T*K/E:
-//   T <= 16:   one 16-row item per touched expert, weights straight into
-//              registers (beam_expert_gemm_direct);
-//   < 256:     mostly one 128-row item per expert, so each weight byte is
-//              streamed once: two 16-row weight tiles per wave, two waves
-//              per SIMD for more bytes in flight (beam_expert_gemm_lds);
-//   >= 256:    several items per expert sharing each weight tile through
-//              L2: four weight tiles per wave, XCD-grouped work order
-//              (beam_expert_gemm_wide), grid rounded to whole XCD rounds.
-enum GemmPath { PATH_DIRECT, PATH_LDS, PATH_WIDE };
-
-static GemmPath gemm_path(int T, int K, int E) {
-    if (T <= 16) return PATH_DIRECT;
-    return (long long)T * K >= 256LL * E ? PATH_WIDE : PATH_LDS;
-}
 
 template <int KIND, bool G1>
 static void launch_gemm(GemmParams p, int n_items_max, GemmPath path, hipStream_t st) {
@@ -824,7 +854,7 @@ hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st) {
                            a.offsets, (const float*)a.wd, a.E, a.H, a.F, a.y, a.y_bf16);
         return hipGetLastError();
     }
-    const int mc = rows_per_item(a.T);
+    const int mc = rows_per_item(a.T, a.K, a.E);
     const int n_items_max = (int)max_items(a.T, a.K, a.E);
     const GemmPath path = gemm_path(a.T, a.K, a.E);
     hipLaunchKernelGGL(beam_build_items, dim3(1), dim3(256), 0, st, a.offsets, a.E, mc, ws.items,

@@ -214,7 +214,8 @@ def _run_experts_stage(wl, T, ids_np, y_dtype):
     ("fp8", torch.bfloat16, 300, 0.5),
     ("f32", torch.float32, 33, 0.5),
     # >= 256 rows per expert on average (T*K >= 256*E): the wide-tile kernel
-    # with several 128-row items per expert and ragged last items
+    # with 256-row items (rows 128..255 included), several per expert, and
+    # ragged last items
     ("bf16", torch.float32, 1500, 0.5),
     ("bf16", torch.bfloat16, 1100, 2.0),
     ("fp8", torch.float32, 1500, 0.5),
