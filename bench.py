@@ -41,6 +41,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 BF16_MFMA_TFLOPS = 2500.0        # dense
 FP8_MFMA_TFLOPS = 5000.0
+SIDE_STREAM_MIN_T = 1024          # tokens from which the input quantisation gets its own stream
 RIDGE_ROWS = 312.5               # rows per expert where weight streaming stops bounding (bf16 and fp8)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 EXPERTS_SRC = os.path.join(ROOT, "expert_routed_ffn_amd", "csrc", "experts.hip")
@@ -127,25 +128,46 @@ def layer_setup(wl, stacks, dev):
     bufs = beam.alloc_buffers(lcfg(wl), wl.T, x.dtype, w_dt, y_dtype=torch.bfloat16 if fp8 else torch.float32,
                               device=dev)
     wgu, wd, sgu, sd = stacks
+    # 8-bit / 4-bit experts at large T: the input quantisation runs on a
+    # second stream (default priority) alongside the router and the
+    # permutation.  At decode sizes the fork and join of a second stream
+    # cost more than the few-µs quantisation they would hide, so it runs in
+    # line there.
+    side = torch.cuda.Stream() if (fp8 or mx) and wl.T >= SIDE_STREAM_MIN_T else None
     return dict(cfg=lcfg(wl), w_r=w_r, bias=bias, x=x, h=h.clone(), h0=h, gp=gp, gq=gq, bufs=bufs,
-                wgu=wgu, wd=wd, sgu=sgu, sd=sd, fp8=fp8, mx=mx)
+                wgu=wgu, wd=wd, sgu=sgu, sd=sd, fp8=fp8, mx=mx, side=side)
 
 
 def run_step(wl, s, hipev=None, evs=None, stream=None):
-    """One layer step through the four C-ABI calls; with evs (5 events) an
-    event is recorded on the launch stream before the first call and after
-    each call."""
+    """One layer step through the C-ABI calls; with evs (5 events) an event
+    is recorded on the launch stream before the first call and after the
+    route, permute, experts and combine_norm calls.  With 8-bit or 4-bit
+    experts the input quantisation runs either on a second stream alongside
+    the route and permute calls (the experts call waits for it) or in line,
+    in the route stage (MXFP4) or inside the permute call (e4m3)."""
+    import torch
     import expert_routed_ffn_amd as beam
     cfg, b = s["cfg"], s["bufs"]
     mark = (lambda i: hipev.record(evs[i], stream)) if evs is not None else (lambda i: None)
+    side = s["side"]
     mark(0)
+    if side is not None:
+        main = torch.cuda.current_stream()
+        side.wait_stream(main)
+        if s["fp8"]:
+            beam.beam_moe_quantize_fp8(cfg, s["x"], b.x_q, b.x_scale, stream=side)
+        else:
+            beam.beam_moe_quantize_mx(cfg, s["x"], b.x_q, b.x_scale, stream=side)
     beam.beam_moe_route(cfg, s["x"], s["w_r"], s["bias"], b.topk_ids, b.topk_w, b.logits, b.ws)
-    if s["mx"]:   # run-time input quantisation of the 4-bit experts (timed in the route stage)
+    if s["mx"] and side is None:   # in line: timed in the route stage
         beam.beam_moe_quantize_mx(cfg, s["x"], b.x_q, b.x_scale)
     mark(1)
+    inline8 = s["fp8"] and side is None   # in line: inside the permute call
     beam.beam_moe_permute(cfg, b.topk_ids, b.expert_offsets, b.row_token, b.pair_row,
-                          x=s["x"] if s["fp8"] else None, x_q=b.x_q if s["fp8"] else None,
-                          x_scale=b.x_scale if s["fp8"] else None, ws=b.ws)
+                          x=s["x"] if inline8 else None, x_q=b.x_q if inline8 else None,
+                          x_scale=b.x_scale if inline8 else None, ws=b.ws)
+    if side is not None:
+        main.wait_stream(side)
     mark(2)
     beam.beam_moe_experts(cfg, wl.T, b.x_q if (s["fp8"] or s["mx"]) else s["x"], b.expert_offsets, b.row_token,
                           s["wgu"], s["wd"], b.y, x_scale=b.x_scale, s_gate_up=s["sgu"], s_down=s["sd"],

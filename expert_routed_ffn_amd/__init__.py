@@ -28,7 +28,7 @@ BEAM_F32, BEAM_BF16, BEAM_FP8_E4M3, BEAM_MXFP4 = 0, 1, 2, 3
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape or dtype",
           3: "workspace missing or too small", 4: "HIP launch failed"}
 
-SYMBOLS = ("beam_moe_route", "beam_moe_permute", "beam_moe_quantize_mx", "beam_moe_experts",
+SYMBOLS = ("beam_moe_route", "beam_moe_permute", "beam_moe_quantize_fp8", "beam_moe_quantize_mx", "beam_moe_experts",
            "beam_moe_experts_static", "beam_moe_combine_norm", "beam_moe_norm_boundary",
            "beam_moe_permute_shard", "beam_moe_combine_partial", "beam_moe_dense_mlp",
            "beam_moe_dense_workspace_bytes", "beam_moe_pack_weights", "beam_moe_workspace_bytes",
@@ -88,6 +88,7 @@ def lib() -> ctypes.CDLL:
                                    vp, sz, vp]
     L.beam_moe_experts_static.argtypes = [cfgp, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp]
     L.beam_moe_quantize_mx.argtypes = [cfgp, i32, vp, i32, vp, vp, vp]
+    L.beam_moe_quantize_fp8.argtypes = [cfgp, i32, vp, i32, vp, vp, vp]
     L.beam_moe_norm_boundary.argtypes = [cfgp, i32, vp, i32, vp, vp, i32, vp, vp, i32, vp]
     L.beam_moe_permute_shard.argtypes = [cfgp, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     L.beam_moe_combine_partial.argtypes = [cfgp, i32, vp, i32, vp, vp, vp, vp]
@@ -196,6 +197,18 @@ def beam_moe_permute(cfg: LayerCfg, topk_ids, expert_offsets, row_token, pair_ro
                                 _p(x_scale), _p(ws), 0 if ws is None else ws.numel(),
                                 _stream(stream))
     _ok("beam_moe_permute", st)
+
+
+def beam_moe_quantize_fp8(cfg: LayerCfg, x, x_q, x_scale, stream=None):
+    """Dynamic per-token e4m3 quantisation of x [T,H] (bf16) into codes x_q
+    [T,H] (uint8/float8_e4m3fn) and fp32 scales x_scale [T]."""
+    T, H = x.shape[0], cfg.hidden
+    _check(x, (T, H), (torch.bfloat16,), "x")
+    _check(x_q, (T, H), (torch.uint8, torch.float8_e4m3fn), "x_q")
+    _check(x_scale, (T,), (torch.float32,), "x_scale")
+    st = lib().beam_moe_quantize_fp8(ctypes.byref(cfg.c()), T, _p(x), _dt(x), _p(x_q), _p(x_scale),
+                                     _stream(stream))
+    _ok("beam_moe_quantize_fp8", st)
 
 
 def beam_moe_quantize_mx(cfg: LayerCfg, x, x_q, x_scale, stream=None):
@@ -440,20 +453,40 @@ def alloc_buffers(cfg: LayerCfg, T: int, act_dtype, w_dtype: int, y_dtype=torch.
 
 
 def moe_layer(cfg: LayerCfg, x, w_router, bias, w_gate_up, w_down, h, gamma_post, gamma_pre, n,
-              bufs: LayerBuffers, s_gate_up=None, s_down=None, stream=None):
-    """Runs the four entry points in order on one stream.  w_gate_up/w_down
-    are packed stacks (beam_moe_pack_weights).  h is updated in place; the
-    other results land in `bufs`."""
+              bufs: LayerBuffers, s_gate_up=None, s_down=None, stream=None, quant_stream=None):
+    """Runs the entry points of one layer in order on one stream.
+    w_gate_up/w_down are packed stacks (beam_moe_pack_weights).  h is
+    updated in place; the other results land in `bufs`.
+
+    With 8-bit or 4-bit experts and a `quant_stream` (a torch.cuda.Stream
+    of the default priority), the input quantisation runs on that stream
+    alongside the router and the permutation, and the experts call waits for
+    it; `stream` is then None (the current stream) or a torch.cuda.Stream.
+    On MI355X that pays off for large batches (fp8, 16384 tokens: about
+    60 µs per layer); at decode sizes the fork and join cost more than the
+    quantisation they hide, so leave quant_stream None there."""
     T = x.shape[0]
     w_dt = _w_dtype(w_gate_up, s_gate_up)
     fp8 = w_dt == BEAM_FP8_E4M3
     mx = w_dt == BEAM_MXFP4
+    side = quant_stream if (fp8 or mx) else None
+    main = None
+    if side is not None:
+        main = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.current_stream()
+        side.wait_stream(main)
+        if fp8:
+            beam_moe_quantize_fp8(cfg, x, bufs.x_q, bufs.x_scale, side)
+        else:
+            beam_moe_quantize_mx(cfg, x, bufs.x_q, bufs.x_scale, side)
     beam_moe_route(cfg, x, w_router, bias, bufs.topk_ids, bufs.topk_w, bufs.logits, bufs.ws, stream)
-    if mx:
+    if mx and side is None:
         beam_moe_quantize_mx(cfg, x, bufs.x_q, bufs.x_scale, stream)
+    q_in_permute = fp8 and side is None
     beam_moe_permute(cfg, bufs.topk_ids, bufs.expert_offsets, bufs.row_token, bufs.pair_row,
-                     x=x if fp8 else None, x_q=bufs.x_q if fp8 else None,
-                     x_scale=bufs.x_scale if fp8 else None, ws=bufs.ws, stream=stream)
+                     x=x if q_in_permute else None, x_q=bufs.x_q if q_in_permute else None,
+                     x_scale=bufs.x_scale if q_in_permute else None, ws=bufs.ws, stream=stream)
+    if side is not None:
+        main.wait_stream(side)
     beam_moe_experts(cfg, T, bufs.x_q if (fp8 or mx) else x, bufs.expert_offsets, bufs.row_token,
                      w_gate_up, w_down, bufs.y, x_scale=bufs.x_scale, s_gate_up=s_gate_up,
                      s_down=s_down, ws=bufs.ws, stream=stream)

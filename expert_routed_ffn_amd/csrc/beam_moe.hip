@@ -337,6 +337,21 @@ beam_status beam_moe_pack_weights(const beam_moe_cfg* cfg, int32_t n_experts, be
     return err == hipSuccess ? BEAM_OK : BEAM_ERR_HIP;
 }
 
+beam_status beam_moe_quantize_fp8(const beam_moe_cfg* cfg, int32_t T, const void* x, beam_dtype x_dtype,
+                                  uint8_t* x_q, float* x_scale, void* stream) {
+    beam_status st = check_cfg(cfg);
+    if (st != BEAM_OK) return st;
+    if (T < 0 || T > kMaxT) return BEAM_ERR_INVALID_ARG;
+    if (x_dtype != BEAM_BF16) return BEAM_ERR_INVALID_ARG;
+    if (T == 0) return BEAM_OK;
+    if (!x || !x_q || !x_scale) return BEAM_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(x_q)) return BEAM_ERR_INVALID_ARG;
+    return beam::launch_quantize_x_e4m3(static_cast<const uint16_t*>(x), T, cfg->hidden, x_q, x_scale,
+                                        static_cast<hipStream_t>(stream)) == hipSuccess
+               ? BEAM_OK
+               : BEAM_ERR_HIP;
+}
+
 beam_status beam_moe_quantize_mx(const beam_moe_cfg* cfg, int32_t T, const void* x, beam_dtype x_dtype,
                                  uint8_t* x_q, uint8_t* x_scale, void* stream) {
     beam_status st = check_cfg(cfg);

@@ -15,7 +15,7 @@
 namespace beam {
 
 constexpr int kMaxIt = 8;    // chunks of 4 per thread: H <= 8 * 1024
-constexpr int kRowGroup = 4; // expert rows whose loads are issued together
+constexpr int kSmallT = 256; // up to this many tokens the grid is too small to hide latency
 
 // 4 consecutive elements as fp32
 template <bool BF> BEAM_DEV float4 ld4(const void* p, size_t i) {
@@ -46,7 +46,12 @@ BEAM_DEV float4 fma4(float w, float4 y, float4 m) {
 }
 
 // One workgroup per token; thread i owns the 4-element chunks i, i+256, ...
-template <bool YBF, bool ABF, int NIT>
+// RG expert rows have their loads issued together.  With few tokens (a
+// grid of T workgroups cannot hide memory latency) RG covers all K rows and
+// h and both gammas are loaded up front, so the kernel makes two round
+// trips to memory instead of five; with many tokens a smaller RG leaves
+// registers for more resident waves.
+template <bool YBF, bool ABF, int NIT, int RG>
 __global__ __launch_bounds__(256) void beam_combine_norm(CombineArgs a) {
     __shared__ float red[4];
     const int t = blockIdx.x, tid = threadIdx.x;
@@ -58,25 +63,41 @@ __global__ __launch_bounds__(256) void beam_combine_norm(CombineArgs a) {
     const int32_t* prow = a.pair_row ? a.pair_row + (size_t)t * K : nullptr;
     const float* wrow = a.w ? a.w + (size_t)t * K : nullptr;
 
+    const size_t rowo = (size_t)t * H;
+    constexpr bool kEager = RG >= 8;
+    float4 hv[kEager ? NIT : 1], gpo[kEager ? NIT : 1], gpr[kEager ? NIT : 1];
+    if constexpr (kEager) {
+        if (!a.partial_only) {
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) {
+                const int i = (it * 256 + tid) * 4;
+                if (i < H) {
+                    hv[it] = ld4<ABF>(a.h, rowo + i);
+                    gpo[it] = ld4<ABF>(a.gpost, i);
+                    gpr[it] = ld4<ABF>(a.gpre, i);
+                }
+            }
+        }
+    }
     float4 m[NIT];
 #pragma unroll
     for (int it = 0; it < NIT; ++it) m[it] = make_float4(0.f, 0.f, 0.f, 0.f);
-    // K expert rows, kRowGroup at a time: indices and weights first, then
-    // every row load of the group in flight together; dropped pairs
-    // (pair_row -1) and anything outside y are skipped
-    for (int k0 = 0; k0 < K; k0 += kRowGroup) {
-        int rr[kRowGroup];
-        float wk[kRowGroup];
+    // K expert rows, RG at a time: indices and weights first, then every
+    // row load of the group in flight together; dropped pairs (pair_row -1)
+    // and anything outside y are skipped
+    for (int k0 = 0; k0 < K; k0 += RG) {
+        int rr[RG];
+        float wk[RG];
 #pragma unroll
-        for (int j = 0; j < kRowGroup; ++j) {
+        for (int j = 0; j < RG; ++j) {
             const int k = k0 + j;
             const int r = k < K ? (prow ? prow[k] : t) : -1;
             rr[j] = ((unsigned)r < (unsigned)TK) ? r : -1;   // never read outside y
             wk[j] = k < K ? (wrow ? wrow[k] : 1.0f) : 0.f;
         }
-        float4 yv[kRowGroup][NIT];
+        float4 yv[RG][NIT];
 #pragma unroll
-        for (int j = 0; j < kRowGroup; ++j)
+        for (int j = 0; j < RG; ++j)
 #pragma unroll
             for (int it = 0; it < NIT; ++it) {
                 const int i = (it * 256 + tid) * 4;
@@ -84,13 +105,12 @@ __global__ __launch_bounds__(256) void beam_combine_norm(CombineArgs a) {
                                                   : make_float4(0.f, 0.f, 0.f, 0.f);
             }
 #pragma unroll
-        for (int j = 0; j < kRowGroup; ++j)
+        for (int j = 0; j < RG; ++j)
 #pragma unroll
             for (int it = 0; it < NIT; ++it) m[it] = fma4(wk[j], yv[j][it], m[it]);
     }
 
     if (a.partial_only) {   // one expert-parallel shard's share of m: no norm
-        const size_t rowo = (size_t)t * H;
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             const int i = (it * 256 + tid) * 4;
@@ -109,15 +129,14 @@ __global__ __launch_bounds__(256) void beam_combine_norm(CombineArgs a) {
     const float rinv = 1.0f / sqrtf(ss / (float)H + a.eps);
 
     // residual update; h' replaces m
-    const size_t rowo = (size_t)t * H;
     float ss2 = 0.f;
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
         const int i = (it * 256 + tid) * 4;
         if (i < H) {
             if (a.moe_out) *reinterpret_cast<float4*>(a.moe_out + rowo + i) = m[it];
-            const float4 g = ld4<ABF>(a.gpost, i);
-            const float4 h = ld4<ABF>(a.h, rowo + i);
+            const float4 g = kEager ? gpo[kEager ? it : 0] : ld4<ABF>(a.gpost, i);
+            const float4 h = kEager ? hv[kEager ? it : 0] : ld4<ABF>(a.h, rowo + i);
             float4 hn;
             hn.x = rnd_act<ABF>(a.c_res * h.x + a.c_new * rnd_act<ABF>(m[it].x * rinv * g.x));
             hn.y = rnd_act<ABF>(a.c_res * h.y + a.c_new * rnd_act<ABF>(m[it].y * rinv * g.y));
@@ -134,7 +153,7 @@ __global__ __launch_bounds__(256) void beam_combine_norm(CombineArgs a) {
         const int i = (it * 256 + tid) * 4;
         if (i < H) {
             st4<ABF>(a.h, rowo + i, m[it]);
-            const float4 g = ld4<ABF>(a.gpre, i);
+            const float4 g = kEager ? gpr[kEager ? it : 0] : ld4<ABF>(a.gpre, i);
             st4<ABF>(a.x_next, rowo + i,
                      make_float4(m[it].x * rinv2 * g.x, m[it].y * rinv2 * g.y, m[it].z * rinv2 * g.z,
                                  m[it].w * rinv2 * g.w));
@@ -142,16 +161,22 @@ __global__ __launch_bounds__(256) void beam_combine_norm(CombineArgs a) {
     }
 }
 
-template <int NIT>
-static void launch_nit(const CombineArgs& a, hipStream_t st) {
+template <int NIT, int RG>
+static void launch_rg(const CombineArgs& a, hipStream_t st) {
     dim3 grid(a.T), block(256);
     if (a.y_bf16) {
-        if (a.act_bf16) hipLaunchKernelGGL((beam_combine_norm<true, true, NIT>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((beam_combine_norm<true, false, NIT>), grid, block, 0, st, a);
+        if (a.act_bf16) hipLaunchKernelGGL((beam_combine_norm<true, true, NIT, RG>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((beam_combine_norm<true, false, NIT, RG>), grid, block, 0, st, a);
     } else {
-        if (a.act_bf16) hipLaunchKernelGGL((beam_combine_norm<false, true, NIT>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((beam_combine_norm<false, false, NIT>), grid, block, 0, st, a);
+        if (a.act_bf16) hipLaunchKernelGGL((beam_combine_norm<false, true, NIT, RG>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((beam_combine_norm<false, false, NIT, RG>), grid, block, 0, st, a);
     }
+}
+
+template <int NIT>
+static void launch_nit(const CombineArgs& a, hipStream_t st) {
+    if (a.T <= kSmallT) launch_rg<NIT, 8>(a, st);
+    else launch_rg<NIT, 4>(a, st);
 }
 
 hipError_t launch_combine_norm(const CombineArgs& a, hipStream_t st) {

@@ -38,6 +38,8 @@ struct PermuteArgs {
 };
 size_t permute_ws_bytes(int T, int K, int E);
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t st);
+// dynamic per-token e4m3 quantisation of bf16 rows x [T,H]
+hipError_t launch_quantize_x_e4m3(const uint16_t* x, int T, int H, uint8_t* xq, float* xscale, hipStream_t st);
 
 enum WKind { W_F32 = 0, W_BF16 = 1, W_FP8 = 2, W_MXFP4 = 3 };
 

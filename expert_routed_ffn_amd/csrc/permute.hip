@@ -172,7 +172,11 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t st) {
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || a.xq == nullptr) return err;
-    hipLaunchKernelGGL(beam_quantize_x_e4m3, dim3(a.T), dim3(256), 0, st, a.x, a.H, a.xq, a.xscale);
+    return launch_quantize_x_e4m3(a.x, a.T, a.H, a.xq, a.xscale, st);
+}
+
+hipError_t launch_quantize_x_e4m3(const uint16_t* x, int T, int H, uint8_t* xq, float* xscale, hipStream_t st) {
+    hipLaunchKernelGGL(beam_quantize_x_e4m3, dim3(T), dim3(256), 0, st, x, H, xq, xscale);
     return hipGetLastError();
 }
 

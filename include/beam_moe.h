@@ -134,6 +134,26 @@ beam_status beam_moe_permute(const beam_moe_cfg* cfg, int32_t T,
                              void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * beam_moe_quantize_fp8 -- dynamic per-token e4m3 quantisation of the layer
+ * input for the FP8 experts, the same codes and scales beam_moe_permute
+ * writes when given x_q.  (Gaudi cookbook, "What was built": dynamic
+ * per-token activation scales; TokenSpeed blog, "TensorRT-LLM NVFP4 MoE":
+ * the input quantisation does not depend on the routes, so it may run on a
+ * second stream of the same priority alongside the router.)
+ *
+ *   x        [T,H] BF16
+ *   x_q      [T,H] out: e4m3 codes, round to nearest even, saturating at
+ *            +-448; 16-byte aligned
+ *   x_scale  [T] out: amax/448 of the row in fp32 (1 for an all-zero row)
+ * T = 0 is a no-op.  NaN elements do not enter the row maximum and get the
+ * e4m3 NaN code; a row holding +-Inf gets an infinite scale, code 0 for its
+ * finite elements and the NaN code for the infinite ones (no fault, no
+ * hang).
+ */
+beam_status beam_moe_quantize_fp8(const beam_moe_cfg* cfg, int32_t T, const void* x, beam_dtype x_dtype,
+                                  uint8_t* x_q, float* x_scale, void* stream);
+
+/*
  * beam_moe_quantize_mx -- run-time MXFP4 quantisation of the layer input for
  * the 4-bit experts.  (TokenSpeed blog, "TensorRT-LLM NVFP4 MoE": the 4-bit
  * MoE quantises its input at run time, a step independent of the routes

@@ -211,3 +211,19 @@ def test_shard_dense_norm_checks(L):
     assert L.beam_moe_dense_workspace_bytes(ctypes.byref(c), 8, 20480) >= 8 * 20480 * 2 + 8 * 8 * 5120 * 4
     assert L.beam_moe_dense_workspace_bytes(ctypes.byref(c), 8, 2560) > 0
     assert L.beam_moe_dense_workspace_bytes(ctypes.byref(c), 8, 100) == 0
+
+
+def test_quantize_argument_checks(L):
+    c = _cfg()
+    # e4m3 input quantisation: bf16 input, codes and scales required, codes 16-byte aligned
+    q8 = lambda T=8, x=FAKE, dt=1, xq=FAKE, xs=FAKE: L.beam_moe_quantize_fp8(ctypes.byref(c), T, x, dt, xq, xs,
+                                                                             None)
+    assert q8(T=0, x=None, xq=None, xs=None) == 0
+    assert q8(T=-1) == 1
+    assert q8(dt=0) == 1
+    assert q8(xs=None) == 1
+    assert q8(xq=FAKE + 4) == 1
+    # MXFP4 input quantisation: bf16 or fp32 input, hidden a multiple of 512
+    qm = lambda T=8, dt=1, cfg=c: L.beam_moe_quantize_mx(ctypes.byref(cfg), T, FAKE, dt, FAKE, FAKE, None)
+    assert qm(dt=2) == 1
+    assert qm(cfg=_cfg(hidden=5184, n_experts=256)) == 2

@@ -312,6 +312,51 @@ def run_graph_replay(wname):
     del g
 
 
+def run_side_stream(wl):
+    """8-bit / 4-bit experts with the input quantisation on a second stream
+    (default priority) beside the router and the permutation: the layer is
+    bit-identical to the one-stream layer, eagerly and in a captured graph
+    replayed twice."""
+    cfg = beam.LayerCfg(wl.hidden, wl.n_experts, wl.n_groups, wl.topk_groups, wl.topk,
+                        wl.group_topn, wl.d_ff, wl.routed_scale, wl.rms_eps)
+    wgu, wd, sgu, sd = stacks(wl, cfg)
+    w_r, bias = synth.make_router(wl, DEV)
+    x, h0, gp, gq = synth.make_activations(wl, DEV)
+    fp8 = wl.w_dtype == "fp8"
+    w_dt = beam.BEAM_FP8_E4M3 if fp8 else beam.BEAM_MXFP4
+    y_dt = torch.bfloat16 if fp8 else torch.float32
+    bufs = beam.alloc_buffers(cfg, wl.T, x.dtype, w_dt, y_dtype=y_dt, keep_moe_out=True, device=DEV)
+    outs = lambda h: [t.clone() for t in (bufs.topk_ids, bufs.topk_w, bufs.pair_row, bufs.x_q, bufs.x_scale,
+                                          bufs.moe_out, h, bufs.x_next)]
+    h = h0.clone()
+    beam.moe_layer(cfg, x, w_r, bias, wgu, wd, h, gp, gq, wl.n, bufs, s_gate_up=sgu, s_down=sd)
+    torch.cuda.synchronize()
+    want = outs(h)
+    side = torch.cuda.Stream()
+    for b in (bufs.x_q, bufs.x_scale):
+        b.zero_()
+    h = h0.clone()
+    beam.moe_layer(cfg, x, w_r, bias, wgu, wd, h, gp, gq, wl.n, bufs, s_gate_up=sgu, s_down=sd,
+                   quant_stream=side)
+    torch.cuda.synchronize()
+    for a, b in zip(outs(h), want):
+        assert torch.equal(a, b)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        beam.moe_layer(cfg, x, w_r, bias, wgu, wd, h, gp, gq, wl.n, bufs, s_gate_up=sgu, s_down=sd,
+                       quant_stream=side)
+    for rep in range(2):
+        h.copy_(h0)
+        bufs.x_q.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs(h), want):
+            assert torch.equal(a, b), rep
+    say(f"  {wl.name} T={wl.T}: quantisation on a second stream, eager and 2 graph replays bit-identical")
+    del g
+
+
 def test_layer_tiny_fp32():
     run_layer("tiny_fp32", 4)
 
@@ -359,7 +404,15 @@ def test_layer_skew_t64_mxfp4():
     run_layer("skew_t64_mxfp4", 64)
 
 
+def test_layer_side_stream_mxfp4():
+    run_side_stream(synth.WORKLOADS["decode_t8_mxfp4"])
+
+
 def test_layer_special_rows_fp8():
     run_special_rows(synth.WORKLOADS["prefill_fp8_t16384"].with_T(8))
+
+
+def test_layer_side_stream_fp8():
+    run_side_stream(synth.WORKLOADS["prefill_fp8_t16384"].with_T(300))
     _stacks.clear()
     torch.cuda.empty_cache()

@@ -137,7 +137,12 @@ def test_quantize_x_e4m3_bit_exact():
     xq = torch.empty((T, H), dtype=torch.uint8, device=DEV)
     xs = torch.empty(T, dtype=torch.float32, device=DEV)
     beam.beam_moe_permute(cfg, ids, off, rt, pr, x=x, x_q=xq, x_scale=xs)
+    # the stand-alone entry point (the one a second stream runs beside the
+    # router) writes the same codes and scales
+    xq2, xs2 = torch.empty_like(xq), torch.empty_like(xs)
+    beam.beam_moe_quantize_fp8(cfg, x, xq2, xs2)
     torch.cuda.synchronize()
+    assert torch.equal(xq2, xq) and torch.equal(xs2, xs)
     xn = synth.to_f64(x)
     q_gpu = oracle.e4m3_decode(xq.cpu().numpy())
     s_gpu = xs.cpu().double().numpy()
