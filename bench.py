@@ -13,6 +13,8 @@ under 8-way expert parallelism (T = 8 and 2048) under "configs".  Prints
 one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--configs a,b|none]
+    (--workload dense_t8 / dense_t2048 / ep8_shard_t8 / ep8_shard_t2048 prints
+    that row's entry alone, for profiling runs)
 
 Timing: HIP events recorded on the launch stream around every C-ABI call
 of every timed step (route, permute, experts, combine_norm), plus one pair
@@ -251,15 +253,15 @@ def algorithmic(wl, D):
                 experts_flops=experts_flops, layer_flops=experts_flops + 2 * T * H * E)
 
 
-def traffic_for(workload):
-    """Measured HBM bytes per beam_moe_experts call from the committed
-    rocprofv3 counter summary, or None if it is missing or was taken on a
-    different expert-kernel source."""
+def traffic_for(workload, call="experts"):
+    """Measured HBM bytes per beam_moe_experts (or beam_moe_dense_mlp) call
+    from the committed rocprofv3 counter summary, or None if it is missing
+    or was taken on a different expert-kernel source."""
     try:
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    rec = t.get(workload, {}).get("experts")
+    rec = t.get(workload, {}).get(call)
     if not rec or rec.get("kernel_src_hash") != kernel_hash():
         return None
     return rec.get("bytes_per_call")
@@ -391,7 +393,8 @@ def time_dense(wl, steps, warmup, hipev, dev):
         ach = wbytes / (mlp_us / 1e6) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "algorithmic_bytes": wbytes}
-    roof.update({"kernel": "beam_moe_dense_mlp call (GEMM1 + SwiGLU, GEMM2" +
+    roof.update({"traffic": traffic_for(wl.name, "dense_mlp"),
+                 "kernel": "beam_moe_dense_mlp call (GEMM1 + SwiGLU, GEMM2" +
                  (", K-slice sum" if T <= 16 else "") + ")", "kernel_avg_us": round(mlp_us, 2)})
     return {"us_per_layer": round(us, 1), "tokens_per_s": round(T / (us / 1e6), 1), "T": T, "d_ff": Fd,
             "expert_weights": "bf16 (dense)", "layer_us": stats(layer),
@@ -457,6 +460,7 @@ def time_ep_shards(wl, stacks, steps, warmup, hipev, dev, n_shards=8):
             "roofline": {"bound": "hbm", "achieved": round(ach / (worst["experts_us"] / 1e6) / 1e9, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": worst["experts_hbm_frac"], "algorithmic_bytes": ach,
+                         "traffic": None,   # counters are taken per layer workload, not per shard
                          "kernel": f"beam_moe_experts call of the slowest shard ({worst['shard']})",
                          "kernel_avg_us": worst["experts_us"]},
             "per_shard": shards}
@@ -506,6 +510,17 @@ def main():
     torch.cuda.set_device(0)
     hipev = HipEvents()
 
+    EP_BASE = {"ep8_shard_t8": "decode_t8", "ep8_shard_t2048": "prefill_t2048"}
+    if args.workload in EP_BASE or synth.WORKLOADS[args.workload].dense:
+        # one dense-layer or EP8-shard row on its own (for profiling runs):
+        # its entry as one JSON line, not the metric line
+        if args.workload in EP_BASE:
+            w1 = synth.WORKLOADS[EP_BASE[args.workload]]
+            e1 = time_ep_shards(w1, packed_stacks(w1, dev), args.steps, args.warmup, hipev, dev)
+        else:
+            e1 = time_dense(synth.WORKLOADS[args.workload], args.steps, args.warmup, hipev, dev)
+        print(json.dumps({"workload": args.workload, **e1}), flush=True)
+        return
     wl = synth.WORKLOADS[args.workload]
     by_dtype = {wl.w_dtype: packed_stacks(wl, dev)}
     r = time_workload(wl, by_dtype[wl.w_dtype], args.steps, args.warmup, hipev, dev, graph=not args.no_graph)

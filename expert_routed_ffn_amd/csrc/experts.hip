@@ -122,7 +122,8 @@ struct GemmParams {
     const float* wscale;       // fp8: per output row
     const uint8_t* mx_act;     // MXFP4: E8M0 codes of the activation rows [rows, K/32]
     const uint8_t* mx_w;       // MXFP4: E8M0 codes of the weight rows [E, rows, K/32]
-    int ksplit;                // GEMM2 on the direct kernel: K slices (gridDim.y)
+    int ksplit;                // direct kernel: K slices (gridDim.y); GEMM1 then
+                               // stores raw gate/up sums, fp32 [row][2F] per slice
     size_t out_slice;          // elements between the fp32 outputs of two slices
     int H, F;
     void* out;
@@ -292,13 +293,17 @@ BEAM_DEV void gemm_item_direct(const GemmParams& p, int e, int row0, int rows, i
         if (has1) compute(1);
     }
     if (!bval) return;
-    if constexpr (!G1) {
-        if (p.ksplit > 1) {   // partial sums of this K slice to its own fp32 output
+    if (p.ksplit > 1) {   // partial sums of this K slice to its own fp32 output
+        if constexpr (G1) {   // raw gate (row a0 + 4g + i) and up (a1 + 4g + i) sums
+            float* o = static_cast<float*>(p.out) + blockIdx.y * p.out_slice + (size_t)(row0 + r) * 2 * p.F;
+            *reinterpret_cast<float4*>(o + a0 + 4 * g) = make_float4(acc0[0], acc0[1], acc0[2], acc0[3]);
+            *reinterpret_cast<float4*>(o + a1 + 4 * g) = make_float4(acc1[0], acc1[1], acc1[2], acc1[3]);
+        } else {
             GemmParams q = p;
             q.out = static_cast<float*>(p.out) + blockIdx.y * p.out_slice;
             store_block<KIND, G1>(q, e, a0, a1, (size_t)row0 + r, tok, acc0, acc1);
-            return;
         }
+        return;
     }
     store_block<KIND, G1>(p, e, a0, a1, (size_t)row0 + r, tok, acc0, acc1);
 }
@@ -700,6 +705,28 @@ __global__ __launch_bounds__(256) void beam_quantize_a_e4m3(const float* __restr
     quantize_row_e4m3(load4, F, aq + row * F, ascale + row, red);
 }
 
+// SwiGLU of K-split GEMM1 sums: a[r][f] = bf16(silu(sum_s g) * sum_s v), the
+// slices added in order (deterministic); g = parts[s][r][f], v = parts[s][r][F + f].
+__global__ __launch_bounds__(256) void beam_swiglu_slices(const float* __restrict__ parts, int S, int rows,
+                                                          int F, uint16_t* __restrict__ a) {
+    const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;   // element of a, F % 4 == 0
+    if (i >= (size_t)rows * F) return;
+    const size_t r = i / F, f = i - r * F;
+    const size_t stride = (size_t)rows * 2 * F;
+    const float* pg = parts + r * 2 * F + f;
+    float4 gs = *reinterpret_cast<const float4*>(pg);
+    float4 vs = *reinterpret_cast<const float4*>(pg + F);
+    for (int s = 1; s < S; ++s) {
+        const float4 gv = *reinterpret_cast<const float4*>(pg + s * stride);
+        const float4 uv = *reinterpret_cast<const float4*>(pg + s * stride + F);
+        gs.x += gv.x; gs.y += gv.y; gs.z += gv.z; gs.w += gv.w;
+        vs.x += uv.x; vs.y += uv.y; vs.z += uv.z; vs.w += uv.w;
+    }
+    const uint32_t lo = f32_to_bf16(silu_f32(gs.x) * vs.x) | (uint32_t(f32_to_bf16(silu_f32(gs.y) * vs.y)) << 16);
+    const uint32_t hi = f32_to_bf16(silu_f32(gs.z) * vs.z) | (uint32_t(f32_to_bf16(silu_f32(gs.w) * vs.w)) << 16);
+    *reinterpret_cast<uint2*>(a + i) = make_uint2(lo, hi);
+}
+
 // ---------------------------------------------------------------- fp32 path
 // One workgroup per permuted row; plain fp32 FMA dot products.
 
@@ -838,7 +865,7 @@ static void launch_gemm(GemmParams p, int n_items_max, GemmPath path, hipStream_
     }
     p.n_tiles = G1 ? F / 64 : H / 128;
     if (path == PATH_DIRECT)
-        hipLaunchKernelGGL((beam_expert_gemm_direct<KIND, G1>), dim3(n_items_max * p.n_tiles, G1 ? 1 : p.ksplit),
+        hipLaunchKernelGGL((beam_expert_gemm_direct<KIND, G1>), dim3(n_items_max * p.n_tiles, p.ksplit),
                            dim3(256), 0, st, p);
     else
         hipLaunchKernelGGL((beam_expert_gemm_lds<KIND, G1>), dim3(n_items_max * p.n_tiles), dim3(256), 0, st, p);
@@ -882,7 +909,17 @@ hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st) {
         p.mx_w = static_cast<const uint8_t*>(a.sgu);
         launch_gemm<W_MXFP4, true>(p, n_items_max, path, st);
     } else if (a.w == W_BF16) {
-        launch_gemm<W_BF16, true>(p, n_items_max, path, st);
+        if (path == PATH_DIRECT && a.ksplit1 > 1) {   // raw sums per K slice, then SwiGLU
+            p.ksplit = a.ksplit1;
+            p.out = a.g1_parts;
+            p.out_slice = (size_t)TK * 2 * a.F;
+            launch_gemm<W_BF16, true>(p, n_items_max, path, st);
+            hipLaunchKernelGGL(beam_swiglu_slices, dim3((unsigned)(((size_t)TK * a.F / 4 + 255) / 256)), dim3(256),
+                               0, st, a.g1_parts, a.ksplit1, TK, a.F, static_cast<uint16_t*>(ws.a));
+            p.ksplit = 1;
+        } else {
+            launch_gemm<W_BF16, true>(p, n_items_max, path, st);
+        }
     } else {
         launch_gemm<W_FP8, true>(p, n_items_max, path, st);
     }

@@ -61,6 +61,11 @@ struct ExpertsArgs {
     // only); slice s writes its partial sums to y + s * y_slice_stride
     int ksplit = 1;
     size_t y_slice_stride = 0;
+    // split of the gate/up projection's K (bf16, direct kernel only): slice s
+    // writes the raw gate and up sums of row r to g1_parts[s][r][0:2F]
+    // (fp32), and a fixed-order sum over the slices applies SwiGLU
+    int ksplit1 = 1;
+    float* g1_parts = nullptr;
 };
 size_t experts_ws_bytes(int T, int K, int E, int H, int F, WKind w);
 hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st);

@@ -22,26 +22,30 @@ template <> BEAM_DEV float4 ld_x4<uint16_t>(const uint16_t* p) {
 }
 
 // ---------------------------------------------------------------------------
-// Small-batch logits (T <= kSmallT): one workgroup per expert streams that
-// expert's router row once and forms the dot products of all tokens with it
-// (the pages' <=16-token GEMV design, re-tiled for 256-thread workgroups).
+// Small-batch logits (T <= kSmallT): workgroup (e, s) streams slice s of
+// expert e's router row once and forms the partial dot products of all
+// tokens with it (the pages' <=16-token GEMV design, re-tiled for
+// 256-thread workgroups and split over K so that each thread has little
+// serial work); the selection kernel adds the slices in slice order.
 // ---------------------------------------------------------------------------
 constexpr int kSmallT = 16;
 
 template <typename XT>
 __global__ __launch_bounds__(256) void beam_router_logits_small(
     const XT* __restrict__ x, const float* __restrict__ w, float* __restrict__ logits,
-    int T, int H, int E) {
-    constexpr int kMaxIt = 8;   // H <= 8 * 1024
+    int T, int H, int E, int kslice) {
+    constexpr int kMaxIt = 8;   // kslice <= 8 * 1024
     __shared__ float red[4][kSmallT];
     const int e = blockIdx.x;
+    const int k0 = blockIdx.y * kslice, k1 = k0 + kslice;
     const float* wr = w + (size_t)e * H;
+    logits += (size_t)blockIdx.y * T * E;
     // all of this thread's router weights first (one latency for the row)
     float4 wv[kMaxIt];
 #pragma unroll
     for (int it = 0; it < kMaxIt; ++it) {
-        const int k = (it * 256 + threadIdx.x) * 4;
-        wv[it] = k < H ? *reinterpret_cast<const float4*>(wr + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+        const int k = k0 + (it * 256 + threadIdx.x) * 4;
+        wv[it] = k < k1 ? *reinterpret_cast<const float4*>(wr + k) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     float acc[kSmallT];
 #pragma unroll
@@ -50,8 +54,8 @@ __global__ __launch_bounds__(256) void beam_router_logits_small(
         if (t < T) {
 #pragma unroll
             for (int it = 0; it < kMaxIt; ++it) {
-                const int k = (it * 256 + threadIdx.x) * 4;
-                if (k < H) {
+                const int k = k0 + (it * 256 + threadIdx.x) * 4;
+                if (k < k1) {
                     const float4 xv = ld_x4<XT>(x + (size_t)t * H + k);
                     acc[t] = fmaf(xv.x, wv[it].x, acc[t]);
                     acc[t] = fmaf(xv.y, wv[it].y, acc[t]);
@@ -404,24 +408,34 @@ int route_splits(int T, int H, int E) {
 
 bool route_uses_mfma(int T, int E, bool x_bf16) { return T > kSmallT && x_bf16 && E % kME == 0; }
 
+// K slices of the small-batch router: four for wide rows (slices of at
+// least 1024 values, a multiple of 4 each), else one
+static int small_splits(int H) { return (H >= 4096 && H % 16 == 0) ? 4 : 1; }
+
+static int route_nsplit(int T, int H, int E, bool x_bf16) {
+    if (T <= kSmallT) return small_splits(H);
+    return route_uses_mfma(T, E, x_bf16) ? route_splits(T, H, E) : 1;
+}
+
 size_t route_partials_bytes(int T, int H, int E) {
-    return (size_t)route_splits(T, H, E) * T * E * sizeof(float);
+    const int s = std::max(route_nsplit(T, H, E, true), route_nsplit(T, H, E, false));
+    return (size_t)s * T * E * sizeof(float);
 }
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
     const int T = a.T, H = a.H, E = a.E;
     // partial logits: the caller's logits_out when there is a single slice,
     // else the workspace
-    int nsplit = 1;
-    if (route_uses_mfma(T, E, a.x_bf16)) nsplit = route_splits(T, H, E);
+    const int nsplit = route_nsplit(T, H, E, a.x_bf16);
     float* part = (nsplit == 1 && a.logits_out) ? a.logits_out : a.partials;
     if (T <= kSmallT) {
+        const dim3 grid(E, nsplit);
         if (a.x_bf16)
-            hipLaunchKernelGGL(beam_router_logits_small<uint16_t>, dim3(E), dim3(256), 0, st,
-                               (const uint16_t*)a.x, a.w, part, T, H, E);
+            hipLaunchKernelGGL(beam_router_logits_small<uint16_t>, grid, dim3(256), 0, st,
+                               (const uint16_t*)a.x, a.w, part, T, H, E, H / nsplit);
         else
-            hipLaunchKernelGGL(beam_router_logits_small<float>, dim3(E), dim3(256), 0, st,
-                               (const float*)a.x, a.w, part, T, H, E);
+            hipLaunchKernelGGL(beam_router_logits_small<float>, grid, dim3(256), 0, st,
+                               (const float*)a.x, a.w, part, T, H, E, H / nsplit);
     } else if (route_uses_mfma(T, E, a.x_bf16)) {
         dim3 grid((T + kMT - 1) / kMT, E / kME, nsplit);
         hipLaunchKernelGGL(beam_router_logits_mfma, grid, dim3(256), 0, st, (const uint16_t*)a.x, a.w,

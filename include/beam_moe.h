@@ -334,8 +334,9 @@ beam_status beam_moe_combine_partial(const beam_moe_cfg* cfg, int32_t T, const v
  *             beam_moe_pack_weights (a cfg with this d_ff, n_experts 1)
  *   y         [T,H] fp32 out
  *   ws        beam_moe_dense_workspace_bytes(cfg, T, d_ff) bytes, 16-byte
- *             aligned; at T <= 16 the down projection is split over K and
- *             its slices are summed in a fixed order (deterministic)
+ *             aligned; at T <= 16 both projections are split over K and
+ *             the slices are summed in a fixed order (deterministic; the
+ *             gate and up sums before SwiGLU is applied)
  */
 beam_status beam_moe_dense_mlp(const beam_moe_cfg* cfg, int32_t T, int32_t d_ff, const void* x,
                                beam_dtype x_dtype, const void* w_gate_up, const void* w_down, float* y,
