@@ -403,13 +403,20 @@ BEAM_DEV void gemm_item_lds(const GemmParams& p, int e, int row0, int rows, int 
             sa1[buf] = ld16(psa1 + k / 16);
         }
     };
-    // one K step on LDS buffer CUR; prefetches step kit+1 into the other buffer
-    auto step = [&](auto curc, int kit) {
+    // one K step on LDS buffer CUR; with PREF it prefetches step kit+1 into
+    // the other buffer.  The loop body always prefetches and the last one or
+    // two steps are peeled off after it: a prefetch under a run-time
+    // condition would make the compiler's wait counts cover both paths, so
+    // the first MFMAs of a step would wait for the loads just issued.
+    auto step = [&](auto curc, auto prefc, int kit) {
         constexpr int CUR = decltype(curc)::value;
-        const bool more = kit + 1 < nk;
-        if (more) {
+        constexpr bool more = decltype(prefc)::value != 0;
+        if constexpr (more) {
             gload((kit + 1) * kKIterBytes);
             aload(CUR ^ 1, (kit + 1) * kKIterBytes);
+            // keep the prefetch at the top of the step (the scheduler would
+            // otherwise sink the activation loads next to their LDS stores)
+            __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
@@ -425,7 +432,7 @@ BEAM_DEV void gemm_item_lds(const GemmParams& p, int e, int row0, int rows, int 
                 mfma_kiter<KIND>(wa1[CUR], xb, acc1[nb]);
             }
         }
-        if (more) swrite(CUR ^ 1);
+        if constexpr (more) swrite(CUR ^ 1);
         __syncthreads();
     };
 
@@ -433,9 +440,16 @@ BEAM_DEV void gemm_item_lds(const GemmParams& p, int e, int row0, int rows, int 
     aload(0, 0);
     swrite(0);
     __syncthreads();
-    for (int kit = 0; kit < nk; kit += 2) {
-        step(IC<0>{}, kit);
-        if (kit + 1 < nk) step(IC<1>{}, kit + 1);
+    int kit = 0;
+    for (; kit + 2 < nk; kit += 2) {
+        step(IC<0>{}, IC<1>{}, kit);
+        step(IC<1>{}, IC<1>{}, kit + 1);
+    }
+    if (kit + 1 < nk) {   // two steps left
+        step(IC<0>{}, IC<1>{}, kit);
+        step(IC<1>{}, IC<0>{}, kit + 1);
+    } else {              // one step left
+        step(IC<0>{}, IC<0>{}, kit);
     }
 
 #pragma unroll
