@@ -648,6 +648,16 @@ BEAM_DEV void gemm_item_wide(const GemmParams& p, int e, int row0, int rows, int
         __syncthreads();
     };
     int kit = 0;
+    if constexpr (KIND == W_BF16) {
+        // four iterations per loop pass: the register shuffle the compiler
+        // puts at the loop head is paid once per four
+        for (; kit + 3 < nk; kit += 4) {
+            body(IC<0>{}, kit);
+            body(IC<1>{}, kit + 1);
+            body(IC<0>{}, kit + 2);
+            body(IC<1>{}, kit + 3);
+        }
+    }
     for (; kit + 1 < nk; kit += 2) {
         body(IC<0>{}, kit);
         body(IC<1>{}, kit + 1);
