@@ -610,7 +610,10 @@ BEAM_DEV void gemm_item_wide(const GemmParams& p, int e, int row0, int rows, int
     constexpr int kReadsPerFrag = KIND == W_BF16 ? 1 : 2;   // 16-byte LDS reads per B fragment
     // instruction classes of the scheduling-group hints
     constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
-    constexpr int LOOK = kLook < NQ ? kLook : NQ;
+    // fp8 fragments are twice as wide: two groups ahead leave the registers
+    // for the four-iteration loop pass
+    constexpr int kLookKind = KIND == W_BF16 ? kLook : 2;
+    constexpr int LOOK = kLookKind < NQ ? kLookKind : NQ;
     auto body = [&](auto curc, int kit) {
         constexpr int cur = decltype(curc)::value;
         const int knext = (kit + 1 < nk ? kit + 1 : kit) * kKIterBytes;
@@ -647,16 +650,14 @@ BEAM_DEV void gemm_item_wide(const GemmParams& p, int e, int row0, int rows, int
         swrite(cur ^ 1);
         __syncthreads();
     };
+    // four iterations per loop pass: the register shuffle the compiler puts
+    // at the loop head is paid once per four; then pairs, then a last one
     int kit = 0;
-    if constexpr (KIND == W_BF16) {
-        // four iterations per loop pass: the register shuffle the compiler
-        // puts at the loop head is paid once per four
-        for (; kit + 3 < nk; kit += 4) {
-            body(IC<0>{}, kit);
-            body(IC<1>{}, kit + 1);
-            body(IC<0>{}, kit + 2);
-            body(IC<1>{}, kit + 3);
-        }
+    for (; kit + 3 < nk; kit += 4) {
+        body(IC<0>{}, kit);
+        body(IC<1>{}, kit + 1);
+        body(IC<0>{}, kit + 2);
+        body(IC<1>{}, kit + 3);
     }
     for (; kit + 1 < nk; kit += 2) {
         body(IC<0>{}, kit);
