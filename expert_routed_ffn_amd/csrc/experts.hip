@@ -284,13 +284,23 @@ BEAM_DEV void gemm_item_direct(const GemmParams& p, int e, int row0, int rows, i
         }
     };
 
+    // every pass of the loop prefetches unconditionally; the last one or two
+    // K iterations are peeled off after it
+    const int nkit = (kbytes - kbeg) / kKIterBytes;
     load(0, kbeg);
-    for (int k = kbeg; k < kbytes; k += 2 * kKIterBytes) {
-        const bool has1 = k + kKIterBytes < kbytes;
-        if (has1) load(1, k + kKIterBytes);
+    int j = 0;
+    for (; j + 2 < nkit; j += 2) {
+        load(1, kbeg + (j + 1) * kKIterBytes);
         compute(0);
-        if (k + 2 * kKIterBytes < kbytes) load(0, k + 2 * kKIterBytes);
-        if (has1) compute(1);
+        load(0, kbeg + (j + 2) * kKIterBytes);
+        compute(1);
+    }
+    if (j + 1 < nkit) {
+        load(1, kbeg + (j + 1) * kKIterBytes);
+        compute(0);
+        compute(1);
+    } else {
+        compute(0);
     }
     if (!bval) return;
     if (p.ksplit > 1) {   // partial sums of this K slice to its own fp32 output
