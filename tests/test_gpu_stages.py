@@ -324,10 +324,12 @@ def test_pack_layout(w_dtype):
 # ------------------------------------------------------------------ combine + norm
 
 @pytest.mark.parametrize("H,K,T,y_dtype,act,n", [
-    (5120, 8, 37, torch.float32, "bf16", 20),
+    (5120, 8, 37, torch.float32, "bf16", 20),      # up to 256 tokens: all K rows per load batch
     (5120, 8, 37, torch.bfloat16, "bf16", 20),
     (5120, 8, 3, torch.float32, "bf16", 1),
     (256, 4, 4, torch.float32, "f32", 5),
+    (5120, 8, 300, torch.float32, "bf16", 20),     # more tokens: one row at a time
+    (5120, 8, 300, torch.bfloat16, "bf16", 20),
 ])
 def test_combine_norm_parity(H, K, T, y_dtype, act, n):
     say(f"combine_norm H={H} K={K} T={T} y={y_dtype} act={act} n={n}")
