@@ -131,6 +131,40 @@ BEAM_DEV void quantize_row_e4m3(Load4 load4, int n, uint8_t* __restrict__ q, flo
     if (threadIdx.x == 0) *scale_out = s;
 }
 
+// The same quantisation of one row by one wave (no barriers): lane l holds
+// the 4-element chunks l, l + 64, ...; NIT >= n / 256 chunks per lane.  The
+// row maximum is exact whatever the reduction order, so the codes and the
+// scale equal those of quantize_row_e4m3.
+template <int NIT, typename Load4>
+BEAM_DEV void quantize_row_e4m3_wave(Load4 load4, int n, uint8_t* __restrict__ q, float* scale_out) {
+    const int lane = threadIdx.x & 63;
+    float v[NIT][4];
+    float amax = 0.f;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int i = (it * 64 + lane) * 4;
+        if (i < n) {
+            const float4 f = load4(i);
+            v[it][0] = f.x; v[it][1] = f.y; v[it][2] = f.z; v[it][3] = f.w;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(v[it][j]));
+        }
+    }
+    amax = wave_max(amax);
+    const float s = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int i = (it * 64 + lane) * 4;
+        if (i < n) {
+            uint32_t c = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) c |= f32_to_e4m3(__fdiv_rn(v[it][j], s)) << (8 * j);
+            *reinterpret_cast<uint32_t*>(q + i) = c;
+        }
+    }
+    if (lane == 0) *scale_out = s;
+}
+
 // Exclusive prefix sum of v over a 256-thread block.  Returns the exclusive
 // value; *total gets the block total.  `tmp` is __shared__ int[4].
 BEAM_DEV int block_exclusive_scan(int v, int* tmp, int* total) {

@@ -738,17 +738,18 @@ __global__ __launch_bounds__(256, 1) void beam_expert_gemm_wide(GemmParams p) {
     else dispatch_wide<KIND, G1, false>(p, it, tile, bs);
 }
 
-// Per-row e4m3 re-quantisation of the fp32 SwiGLU output (fp8 path).
+// Per-row e4m3 re-quantisation of the fp32 SwiGLU output (fp8 path): one
+// wave per row, four rows per workgroup.
+template <int NIT>
 __global__ __launch_bounds__(256) void beam_quantize_a_e4m3(const float* __restrict__ a,
                                                             const int32_t* __restrict__ offsets, int E,
                                                             int F, uint8_t* __restrict__ aq,
                                                             float* __restrict__ ascale) {
-    __shared__ float red[4];
-    const size_t row = blockIdx.x;
-    if (row >= (size_t)offsets[E]) return;
+    const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= (size_t)offsets[E]) return;   // whole wave exits together
     const float* ar = a + row * F;
     auto load4 = [&](int i) { return *reinterpret_cast<const float4*>(ar + i); };
-    quantize_row_e4m3(load4, F, aq + row * F, ascale + row, red);
+    quantize_row_e4m3_wave<NIT>(load4, F, aq + row * F, ascale + row);
 }
 
 // SwiGLU of K-split GEMM1 sums: a[r][f] = bf16(silu(sum_s g) * sum_s v), the
@@ -990,8 +991,23 @@ hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st) {
         p.mx_w = static_cast<const uint8_t*>(a.sd);
         launch_gemm<W_MXFP4, false>(p, n_items_max, path, st);
     } else if (a.w == W_FP8) {
-        hipLaunchKernelGGL(beam_quantize_a_e4m3, dim3(TK), dim3(256), 0, st, (const float*)ws.a,
-                           a.offsets, a.E, a.F, ws.aq, ws.ascale);
+        const dim3 qgrid((TK + 3) / 4);
+        const float* af = static_cast<const float*>(ws.a);
+        if (a.F <= 1024)
+            hipLaunchKernelGGL(beam_quantize_a_e4m3<4>, qgrid, dim3(256), 0, st, af, a.offsets, a.E, a.F, ws.aq,
+                               ws.ascale);
+        else if (a.F <= 2048)
+            hipLaunchKernelGGL(beam_quantize_a_e4m3<8>, qgrid, dim3(256), 0, st, af, a.offsets, a.E, a.F, ws.aq,
+                               ws.ascale);
+        else if (a.F <= 2560)   // the Beam d_ff
+            hipLaunchKernelGGL(beam_quantize_a_e4m3<10>, qgrid, dim3(256), 0, st, af, a.offsets, a.E, a.F, ws.aq,
+                               ws.ascale);
+        else if (a.F <= 4096)
+            hipLaunchKernelGGL(beam_quantize_a_e4m3<16>, qgrid, dim3(256), 0, st, af, a.offsets, a.E, a.F, ws.aq,
+                               ws.ascale);
+        else
+            hipLaunchKernelGGL(beam_quantize_a_e4m3<32>, qgrid, dim3(256), 0, st, af, a.offsets, a.E, a.F, ws.aq,
+                               ws.ascale);
         p.act = ws.aq;
         p.act_scale = ws.ascale;
         launch_gemm<W_FP8, false>(p, n_items_max, path, st);

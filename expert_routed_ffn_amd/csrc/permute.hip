@@ -132,18 +132,20 @@ __global__ __launch_bounds__(kPermThreads) void beam_permute_scatter(
     stable_scatter(ids, e_base, begin, end, K, E, ebits, cursor, row_token, pair_row);
 }
 
-// Dynamic per-token e4m3 quantisation of x: one workgroup per token row.
+// Dynamic per-token e4m3 quantisation of x: one wave per token row, four
+// rows per workgroup.
+template <int NIT>
 __global__ __launch_bounds__(256) void beam_quantize_x_e4m3(
-    const uint16_t* __restrict__ x, int H, uint8_t* __restrict__ xq, float* __restrict__ xscale) {
-    __shared__ float red[4];
-    const size_t row = blockIdx.x;
+    const uint16_t* __restrict__ x, int T, int H, uint8_t* __restrict__ xq, float* __restrict__ xscale) {
+    const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= (size_t)T) return;   // whole wave exits together
     const uint16_t* xr = x + row * H;
     auto load4 = [&](int i) {
         const uint2 u = *reinterpret_cast<const uint2*>(xr + i);
         return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
                            __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
     };
-    quantize_row_e4m3(load4, H, xq + row * H, xscale + row, red);
+    quantize_row_e4m3_wave<NIT>(load4, H, xq + row * H, xscale + row);
 }
 
 static int n_chunks(int TK) { return (TK + kPermChunk - 1) / kPermChunk; }
@@ -176,7 +178,15 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_quantize_x_e4m3(const uint16_t* x, int T, int H, uint8_t* xq, float* xscale, hipStream_t st) {
-    hipLaunchKernelGGL(beam_quantize_x_e4m3, dim3(T), dim3(256), 0, st, x, H, xq, xscale);
+    const dim3 grid((T + 3) / 4);   // H <= 8192: at most 32 chunks of 4 per lane
+    if (H <= 2048)
+        hipLaunchKernelGGL(beam_quantize_x_e4m3<8>, grid, dim3(256), 0, st, x, T, H, xq, xscale);
+    else if (H <= 4096)
+        hipLaunchKernelGGL(beam_quantize_x_e4m3<16>, grid, dim3(256), 0, st, x, T, H, xq, xscale);
+    else if (H <= 5120)   // the Beam hidden size
+        hipLaunchKernelGGL(beam_quantize_x_e4m3<20>, grid, dim3(256), 0, st, x, T, H, xq, xscale);
+    else
+        hipLaunchKernelGGL(beam_quantize_x_e4m3<32>, grid, dim3(256), 0, st, x, T, H, xq, xscale);
     return hipGetLastError();
 }
 
