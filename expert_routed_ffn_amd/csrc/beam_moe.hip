@@ -112,8 +112,7 @@ beam_status experts_prepare(const beam_moe_cfg* cfg, int32_t T, beam_dtype w_dty
     if (y_dtype == BEAM_FP8_E4M3 || y_dtype == BEAM_MXFP4) return BEAM_ERR_INVALID_ARG;
     if (w_dtype == BEAM_FP8_E4M3 && (cfg->hidden % 256 != 0 || cfg->d_ff % 256 != 0))
         return BEAM_ERR_UNSUPPORTED;
-    if (w_dtype == BEAM_MXFP4 && (!mx_shape_ok(cfg) || (int64_t)T * cfg->topk >= 256LL * cfg->n_experts))
-        return BEAM_ERR_UNSUPPORTED;
+    if (w_dtype == BEAM_MXFP4 && !mx_shape_ok(cfg)) return BEAM_ERR_UNSUPPORTED;
     if (T == 0) return BEAM_OK;
     if (!x || !expert_offsets || !row_token || !w_gate_up || !w_down || !y) return BEAM_ERR_INVALID_ARG;
     if ((w_dtype == BEAM_FP8_E4M3 || w_dtype == BEAM_MXFP4) && (!x_scale || !s_gate_up || !s_down))

@@ -543,8 +543,9 @@ BEAM_DEV i32x8 pair8(uint4 lo, uint4 hi) {
 
 template <int KIND, bool G1, int NB, bool NT>
 BEAM_DEV void gemm_item_wide(const GemmParams& p, int e, int row0, int rows, int tile,
-                             uint4 (*bs)[kWideRows * 16]) {
-    constexpr int NS = (KIND == W_BF16) ? 4 : 2;   // MFMA steps per 256-byte K iteration
+                             uint4 (*bs)[kWideRows * 16], uint4* ssc) {
+    constexpr bool MX = KIND == W_MXFP4;
+    constexpr int NS = (KIND == W_FP8) ? 2 : 4;   // MFMA steps per 256-byte K iteration
     const int lane = threadIdx.x & 63;
     const int r = lane & 15, g = lane >> 4;
     const int kbytes = row_bytes<KIND>(G1 ? p.H : p.F);
@@ -565,6 +566,22 @@ BEAM_DEV void gemm_item_wide(const GemmParams& p, int e, int row0, int rows, int
         srow[i] = G1 ? p.row_token[row0 + rr] : row0 + rr;
     }
     const uint8_t* act = p.act + 16 * lc;
+    // MXFP4: the E8M0 codes of the item's activation rows for the whole K
+    // go to LDS once (row rr's 16 codes of K iteration c at ssc[16 rr + c]);
+    // each weight row's 16 codes per K iteration stream with its weights
+    const int kblk = (G1 ? p.H : p.F) / 32;
+    const uint8_t* psw[4] = {nullptr, nullptr, nullptr, nullptr};
+    if constexpr (MX) {
+        for (int q = threadIdx.x; q < kWideRows * nk; q += 256) {
+            const int rr = q / nk, c = q - rr * nk;
+            const int src = rr < rows ? rr : 0;
+            const size_t srow_mx = G1 ? (size_t)p.row_token[row0 + src] : (size_t)(row0 + src);
+            ssc[rr * 16 + c] = ld16(p.mx_act + srow_mx * kblk + c * 16);
+        }
+        const size_t wrow0 = (size_t)e * (G1 ? 2 * p.F : p.H);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) psw[j] = p.mx_w + (wrow0 + a[j] + r) * kblk;
+    }
     uint4 stage[NB];
     auto gload = [&](int k) {
 #pragma unroll
@@ -587,25 +604,47 @@ BEAM_DEV void gemm_item_wide(const GemmParams& p, int e, int row0, int rows, int
     // One set of weight fragments, one register group per MFMA step; the
     // group of step st is reloaded for the next K iteration as soon as the
     // step's last MFMA has issued (one iteration of latency to hide).
-    using WFrag = typename std::conditional<KIND == W_BF16, uint4, i32x8>::type;
+    using WFrag = typename std::conditional<KIND == W_FP8, i32x8, uint4>::type;
     WFrag wa[4][NS];
+    uint4 sw[4];   // MXFP4: the lane's weight rows' 16 E8M0 codes of the K iteration
     auto aload_step = [&](int st, int k) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            if constexpr (KIND == W_BF16) wa[j][st] = wload(j, st, k);
-            else wa[j][st] = pair8(wload(j, 2 * st, k), wload(j, 2 * st + 1, k));
+            if constexpr (KIND == W_FP8) wa[j][st] = pair8(wload(j, 2 * st, k), wload(j, 2 * st + 1, k));
+            else wa[j][st] = wload(j, st, k);
+        }
+        if constexpr (MX) {   // after the iteration's last step: the next iteration's codes
+            if (st == NS - 1) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sw[j] = ld16(psw[j] + k / 16);
+            }
         }
     };
     // B fragment q of a K iteration (q = st * NB + nb): the 16 rows of row
-    // block nb for MFMA step st, from the staged LDS tile
-    auto bload = [&](const uint4* b, int q) -> WFrag {
+    // block nb for MFMA step st, from the staged LDS tile (MXFP4: with the
+    // row's E8M0 word of the step)
+    struct MxB {
+        uint4 v;
+        uint32_t s;
+    };
+    using BFrag = typename std::conditional<MX, MxB, WFrag>::type;
+    auto bload = [&](const uint4* b, int q, int kit) -> BFrag {
         const int st = q / NB, nb = q % NB;
-        if constexpr (KIND == W_BF16) return b[lds_pos(nb * 16 + r, 4 * st + g)];
-        else return pair8(b[lds_pos(nb * 16 + r, 4 * (2 * st) + g)], b[lds_pos(nb * 16 + r, 4 * (2 * st + 1) + g)]);
+        if constexpr (MX)
+            return MxB{b[lds_pos(nb * 16 + r, 4 * st + g)],
+                       reinterpret_cast<const uint32_t*>(ssc)[((nb * 16 + r) * 16 + kit) * 4 + st]};
+        else if constexpr (KIND == W_BF16)
+            return b[lds_pos(nb * 16 + r, 4 * st + g)];
+        else
+            return pair8(b[lds_pos(nb * 16 + r, 4 * (2 * st) + g)], b[lds_pos(nb * 16 + r, 4 * (2 * st + 1) + g)]);
     };
     gload(0);
 #pragma unroll
     for (int st = 0; st < NS; ++st) aload_step(st, 0);
+    if constexpr (MX) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sw[j] = ld16(psw[j]);
+    }
     swrite(0);
     __syncthreads();
     // One straight-line body per LDS buffer, the pair unrolled in the loop
@@ -617,29 +656,39 @@ BEAM_DEV void gemm_item_wide(const GemmParams& p, int e, int row0, int rows, int
     // order.  The last iteration reloads its own K slice (in bounds, never
     // used).
     constexpr int NQ = NS * NB;
-    constexpr int kReadsPerFrag = KIND == W_BF16 ? 1 : 2;   // 16-byte LDS reads per B fragment
+    constexpr int kReadsPerFrag = KIND == W_BF16 ? 1 : 2;   // LDS reads per B fragment
     // instruction classes of the scheduling-group hints
     constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
     // fp8 fragments are twice as wide: two groups ahead leave the registers
     // for the four-iteration loop pass
-    constexpr int kLookKind = KIND == W_BF16 ? kLook : 2;
+    constexpr int kLookKind = KIND == W_FP8 ? 2 : kLook;
     constexpr int LOOK = kLookKind < NQ ? kLookKind : NQ;
     auto body = [&](auto curc, int kit) {
         constexpr int cur = decltype(curc)::value;
         const int knext = (kit + 1 < nk ? kit + 1 : kit) * kKIterBytes;
         gload(knext);
         const uint4* bcur = bs[cur];
-        WFrag xq[LOOK];
+        BFrag xq[LOOK];
 #pragma unroll
-        for (int d = 0; d < LOOK; ++d) xq[d] = bload(bcur, d);
+        for (int d = 0; d < LOOK; ++d) xq[d] = bload(bcur, d, kit);
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, LOOK * kReadsPerFrag, 0);
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             const int st = q / NB, nb = q % NB;
-            const WFrag xb = xq[q % LOOK];
+            const BFrag xb = xq[q % LOOK];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                if constexpr (KIND == W_BF16)
+                if constexpr (MX) {
+                    // formats 4/4 = E2M1 x E2M1 (the low 4 dwords of each
+                    // operand); lane (r, g) takes byte g of the step's words
+                    const uint32_t wsw = st == 0 ? sw[j].x : st == 1 ? sw[j].y : st == 2 ? sw[j].z : sw[j].w;
+                    const int sh = 8 * g;
+                    const i32x8 av = {(int)wa[j][st].x, (int)wa[j][st].y, (int)wa[j][st].z, (int)wa[j][st].w,
+                                      0, 0, 0, 0};
+                    const i32x8 bv = {(int)xb.v.x, (int)xb.v.y, (int)xb.v.z, (int)xb.v.w, 0, 0, 0, 0};
+                    acc[j][nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        av, bv, acc[j][nb], 4, 4, 0, (int)((wsw >> sh) & 0xFF), 0, (int)((xb.s >> sh) & 0xFF));
+                } else if constexpr (KIND == W_BF16)
                     acc[j][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         __builtin_bit_cast(bf16x8, wa[j][st]), __builtin_bit_cast(bf16x8, xb), acc[j][nb], 0, 0, 0);
                 else   // formats 0/0 = e4m3 x e4m3; block scales 127 = 2^0 (unscaled)
@@ -648,7 +697,7 @@ BEAM_DEV void gemm_item_wide(const GemmParams& p, int e, int row0, int rows, int
             }
             __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
             if (q + LOOK < NQ) {
-                xq[q % LOOK] = bload(bcur, q + LOOK);
+                xq[q % LOOK] = bload(bcur, q + LOOK, kit);
                 __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kReadsPerFrag, 0);
             }
             if (nb == NB - 1) {
@@ -704,13 +753,13 @@ BEAM_DEV void gemm_item_wide(const GemmParams& p, int e, int row0, int rows, int
 }
 
 template <int KIND, bool G1, bool NT>
-BEAM_DEV void dispatch_wide(const GemmParams& p, int4 it, int tile, uint4 (*bs)[kWideRows * 16]) {
+BEAM_DEV void dispatch_wide(const GemmParams& p, int4 it, int tile, uint4 (*bs)[kWideRows * 16], uint4* ssc) {
     if (it.z <= 32)
-        gemm_item_wide<KIND, G1, 2, NT>(p, it.x, it.y, it.z, tile, bs);
+        gemm_item_wide<KIND, G1, 2, NT>(p, it.x, it.y, it.z, tile, bs, ssc);
     else if (it.z <= 64)
-        gemm_item_wide<KIND, G1, 4, NT>(p, it.x, it.y, it.z, tile, bs);
+        gemm_item_wide<KIND, G1, 4, NT>(p, it.x, it.y, it.z, tile, bs, ssc);
     else
-        gemm_item_wide<KIND, G1, 8, NT>(p, it.x, it.y, it.z, tile, bs);
+        gemm_item_wide<KIND, G1, 8, NT>(p, it.x, it.y, it.z, tile, bs, ssc);
 }
 
 // Block -> (item, N-tile).  Work units are ordered expert by expert, N-tile
@@ -722,6 +771,8 @@ BEAM_DEV void dispatch_wide(const GemmParams& p, int4 it, int tile, uint4 (*bs)[
 template <int KIND, bool G1>
 __global__ __launch_bounds__(256, 1) void beam_expert_gemm_wide(GemmParams p) {
     __shared__ uint4 bs[2][kWideRows * 16];
+    // MXFP4: the activation rows' E8M0 codes for the whole K (16 per K iteration)
+    __shared__ uint4 ssc[KIND == W_MXFP4 ? kWideRows * 16 : 1];
     const int total = *p.n_items * p.n_tiles;
     const int per_xcd = (total + 7) >> 3;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
@@ -734,8 +785,8 @@ __global__ __launch_bounds__(256, 1) void beam_expert_gemm_wide(GemmParams p) {
     const int local = j - first * p.n_tiles;          // = tile * cnt + item within the expert
     const int tile = local / cnt;
     const int4 it = p.items[first + (local - tile * cnt)];
-    if (cnt == 1) dispatch_wide<KIND, G1, true>(p, it, tile, bs);
-    else dispatch_wide<KIND, G1, false>(p, it, tile, bs);
+    if (cnt == 1) dispatch_wide<KIND, G1, true>(p, it, tile, bs, ssc);
+    else dispatch_wide<KIND, G1, false>(p, it, tile, bs, ssc);
 }
 
 // Per-row e4m3 re-quantisation of the fp32 SwiGLU output (fp8 path): one

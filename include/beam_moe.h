@@ -194,8 +194,7 @@ beam_status beam_moe_quantize_mx(const beam_moe_cfg* cfg, int32_t T, const void*
  *             beam_moe_quantize_mx; the fp32 SwiGLU output a is quantised
  *             the same way (32-element blocks) before GEMM2; all products on
  *             the scaled FP4 x FP4 matrix cores, fp32 accumulation.
- *             Supported for up to 255 rows per expert on average
- *             (T*K < 256*E); larger calls return BEAM_ERR_UNSUPPORTED.
+ *             Requires hidden and d_ff multiples of 512.
  *   x         [T,H] dtype per w_dtype (x_dtype must be F32, BF16, FP8_E4M3
  *             or MXFP4 to match; MXFP4: [T,H/2] bytes); x_scale: FP8 [T]
  *             fp32, MXFP4 [T,H/32] E8M0 codes, else unused

@@ -92,12 +92,16 @@ WORKLOADS = {
     # throughput rather than HBM bandwidth bounds the expert GEMMs
     "prefill_bf16_t16384": Workload("prefill_bf16_t16384", T=16384, n=20, act_dtype="bf16",
                                     w_dtype="bf16", bias_sigma=0.02, seed=1, **_BEAM),
+    # the same prefill shape with 4-bit (MXFP4) experts
+    "prefill_mxfp4_t16384": Workload("prefill_mxfp4_t16384", T=16384, n=20, act_dtype="bf16",
+                                     w_dtype="mxfp4", bias_sigma=0.02, seed=1, **_BEAM),
 }
 # the order the workloads are listed in (index = position in that list; the
 # bf16 16384-token shape, the 4-bit decode shapes and the dense layers came
 # after the first five)
 WORKLOAD_ORDER = ["tiny_fp32", "decode_t8", "skew_t64", "prefill_t2048", "prefill_fp8_t16384",
-                  "prefill_bf16_t16384", "decode_t8_mxfp4", "skew_t64_mxfp4", "dense_t8", "dense_t2048"]
+                  "prefill_bf16_t16384", "decode_t8_mxfp4", "skew_t64_mxfp4", "dense_t8", "dense_t2048",
+                  "prefill_mxfp4_t16384"]
 
 
 def _seed(*parts: int) -> int:

@@ -121,11 +121,11 @@ def test_experts_argument_checks(L):
     assert f(w_dt=7, x_dt=7) == 1
     assert f(T=-1) == 1
     assert f(T=(1 << 22) + 1) == 1             # beyond the largest token count
-    # 4-bit experts: decode-sized batches only (the wide kernel has no MXFP4
-    # path), hidden and d_ff multiples of 512
+    # 4-bit experts: any batch (all three GEMM paths), hidden and d_ff
+    # multiples of 512
     mx = dict(w_dt=3, x_dt=3, xs=FAKE, sgu=FAKE, sd=FAKE)
-    assert f(T=8191, ws=None, **mx) == 3       # 8191 * 8 < 256 * 256: on to the workspace check
-    assert f(T=8192, **mx) == 2
+    assert f(T=8, ws=None, **mx) == 3          # past the shape checks: on to the workspace check
+    assert f(T=16384, ws=None, **mx) == 3
     c2 = _cfg(d_ff=2304)
     assert L.beam_moe_experts(ctypes.byref(c2), 8, 3, FAKE, 3, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                               0, FAKE, 1 << 40, None) == 2

@@ -404,6 +404,13 @@ def test_layer_skew_t64_mxfp4():
     run_layer("skew_t64_mxfp4", 64)
 
 
+@pytest.mark.timeout(400)
+def test_layer_prefill_mxfp4_t16384():
+    # 8 sampled tokens (the oracle decodes every 4-bit expert a token uses);
+    # the heaviest experts are still checked row by row
+    run_layer("prefill_mxfp4_t16384", 8)
+
+
 def test_layer_side_stream_mxfp4():
     run_side_stream(synth.WORKLOADS["decode_t8_mxfp4"])
 

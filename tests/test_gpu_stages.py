@@ -244,6 +244,8 @@ def test_experts_parity(w_dtype, y_dtype, T, skew):
     (torch.bfloat16, 12, 0.0),
     (torch.float32, 300, 0.5),     # 128-row items staged in LDS, ragged tails
     (torch.float32, 37, 3.0),      # heavy skew, empty experts
+    (torch.float32, 1500, 0.5),    # >= 256 rows per expert: the wide-tile kernel
+    (torch.bfloat16, 1100, 2.0),
 ])
 def test_experts_mxfp4_parity(y_dtype, T, skew):
     say(f"experts mxfp4 y={y_dtype} T={T} skew={skew}")
