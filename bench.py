@@ -7,7 +7,7 @@ and all 256 experts' weights resident in HBM.  The headline line is the
 Beam decode shape (T = 8 tokens, bf16 experts); the same JSON line carries
 the other shapes the metric is quoted on (T = 64 with skewed routes,
 T = 2048 prefill, T = 16384 with fp8 experts, and T = 16384 with bf16
-experts), the decode shapes with 4-bit MXFP4 experts (T = 8 and 64), the
+experts), the shapes with 4-bit MXFP4 experts (T = 8, 64 and 16384), the
 dense layers (d_ff 20480, T = 8 and 2048) and one GPU's share of the layer
 under 8-way expert parallelism (T = 8 and 2048) under "configs".  Prints
 one JSON line.
@@ -43,12 +43,23 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 BF16_MFMA_TFLOPS = 2500.0        # dense
 FP8_MFMA_TFLOPS = 5000.0
+FP4_MFMA_TFLOPS = 10100.0
+MFMA_PEAK = {"bf16": BF16_MFMA_TFLOPS, "f32": BF16_MFMA_TFLOPS, "fp8": FP8_MFMA_TFLOPS, "mxfp4": FP4_MFMA_TFLOPS}
+WEIGHT_BYTES = {"bf16": 2.0, "f32": 4.0, "fp8": 1.0, "mxfp4": 0.5 + 1.0 / 32}   # per weight, with block scales
+
+
+def ridge_rows(w_dtype):
+    """Rows per expert at which the expert GEMMs' flops per weight byte
+    reach the MFMA peak over the HBM peak (312.5 for bf16 and fp8, about
+    335 for MXFP4)."""
+    return MFMA_PEAK[w_dtype] * 1e12 / (HBM_PEAK_GBS * 1e9) / (2.0 / WEIGHT_BYTES[w_dtype])
 SIDE_STREAM_MIN_T = 1024          # tokens from which the input quantisation gets its own stream
 RIDGE_ROWS = 312.5               # rows per expert where weight streaming stops bounding (bf16 and fp8)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 EXPERTS_SRC = os.path.join(ROOT, "expert_routed_ffn_amd", "csrc", "experts.hip")
 DEFAULT_CONFIGS = ("skew_t64,prefill_t2048,prefill_fp8_t16384,prefill_bf16_t16384,"
-                   "decode_t8_mxfp4,skew_t64_mxfp4,dense_t8,dense_t2048,ep8_shard_t8,ep8_shard_t2048")
+                   "decode_t8_mxfp4,skew_t64_mxfp4,prefill_mxfp4_t16384,dense_t8,dense_t2048,ep8_shard_t8,"
+                   "ep8_shard_t2048")
 METRIC = "MoE-layer tokens/s (one Beam MoE layer forward incl. routing and norm boundary)"
 
 
@@ -276,8 +287,8 @@ def roofline_entry(wl, r):
     ex_us = sum(r["per"]["experts"]) / len(r["per"]["experts"])
     ex_s = ex_us / 1e6
     rows_per_expert = wl.T * wl.topk / max(D, 1)
-    if rows_per_expert >= RIDGE_ROWS:
-        peak = FP8_MFMA_TFLOPS if fp8 else BF16_MFMA_TFLOPS
+    if rows_per_expert >= ridge_rows(wl.w_dtype):
+        peak = MFMA_PEAK[wl.w_dtype]
         ach = alg["experts_flops"] / ex_s / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(ach / peak, 4), "algorithmic_flops": alg["experts_flops"]}
@@ -291,7 +302,7 @@ def roofline_entry(wl, r):
                            + (", MXFP4 quantisation of a" if mx else "") + ")",
                  "kernel_avg_us": round(ex_us, 2)})
     step_s = r["ms_per_step"] / 1e3
-    peak_f = FP8_MFMA_TFLOPS if fp8 else BF16_MFMA_TFLOPS
+    peak_f = MFMA_PEAK[wl.w_dtype]
     layer = {"hbm_frac": round(alg["layer_bytes"] / step_s / 1e9 / HBM_PEAK_GBS, 4),
              "mfma_frac": round(alg["layer_flops"] / step_s / 1e12 / peak_f, 4),
              "algorithmic_bytes": alg["layer_bytes"], "algorithmic_flops": alg["layer_flops"]}
