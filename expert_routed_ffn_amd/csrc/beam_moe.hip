@@ -32,7 +32,7 @@ beam_status check_cfg(const beam_moe_cfg* c) {
         !isfinite(c->rms_eps))
         return BEAM_ERR_INVALID_ARG;
     if (c->hidden % 256 != 0 || c->hidden > 8192) return BEAM_ERR_UNSUPPORTED;
-    if (c->n_experts > 256 || c->n_experts % c->n_groups != 0) return BEAM_ERR_UNSUPPORTED;
+    if (c->n_experts > beam::kMaxExperts || c->n_experts % c->n_groups != 0) return BEAM_ERR_UNSUPPORTED;
     const int per = c->n_experts / c->n_groups;
     const int epl = epl_of(c->n_experts);
     if (per % epl != 0) return BEAM_ERR_UNSUPPORTED;

@@ -33,8 +33,8 @@ template <bool BF> BEAM_DEV float rnd_act(float v) {
 }
 template <bool BF> BEAM_DEV void st4(void* p, size_t i, float4 v) {
     if constexpr (BF) {
-        const uint32_t a = f32_to_bf16(v.x) | (uint32_t(f32_to_bf16(v.y)) << 16);
-        const uint32_t b = f32_to_bf16(v.z) | (uint32_t(f32_to_bf16(v.w)) << 16);
+        const uint32_t a = pack_bf16x2(v.x, v.y);
+        const uint32_t b = pack_bf16x2(v.z, v.w);
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p) + i) = make_uint2(a, b);
     } else {
         *reinterpret_cast<float4*>(static_cast<float*>(p) + i) = v;

@@ -19,11 +19,15 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 BEAM_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
 // round-to-nearest-even fp32 -> bf16; NaN stays a (quiet) NaN
-BEAM_DEV uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return uint16_t((u >> 16) | 0x40u);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return uint16_t(u >> 16);
+// fp32 -> bf16, round to nearest even (NaN stays NaN): the gfx950
+// conversion instruction
+BEAM_DEV uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f)); }
+
+// two values, lo in the low half (one conversion instruction)
+BEAM_DEV uint32_t pack_bf16x2(float lo, float hi) {
+    typedef float f32x2v __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v{lo, hi}), bf16x2v));
 }
 
 // ---------------------------------------------------------------- e4m3 bits
@@ -90,7 +94,9 @@ BEAM_DEV uint32_t ordered_bits(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-BEAM_DEV float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+// g * sigmoid(g), with the hardware reciprocal (1 ulp) in place of a
+// correctly rounded division
+BEAM_DEV float silu_f32(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 }  // namespace beam
 

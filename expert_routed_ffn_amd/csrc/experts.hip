@@ -43,7 +43,9 @@ BEAM_DEV uint4 ld16_nt(const uint8_t* p) {
 
 __global__ __launch_bounds__(256) void beam_build_items(const int32_t* __restrict__ offsets, int E,
                                                         int MC, int4* __restrict__ items,
-                                                        int* __restrict__ n_items) {
+                                                        int* __restrict__ n_items,
+                                                        int* __restrict__ first_item,
+                                                        int* __restrict__ unit_ctr) {
     __shared__ int tmp[4];
     const int e = threadIdx.x;
     const int cnt = e < E ? offsets[e + 1] - offsets[e] : 0;
@@ -55,7 +57,12 @@ __global__ __launch_bounds__(256) void beam_build_items(const int32_t* __restric
     // workgroups, which should then keep them cacheable
     for (int c = 0; c < nch; ++c)
         items[first + c] = make_int4(e, offsets[e] + c * MC, min(MC, cnt - c * MC), (c << 16) | nch);
-    if (e == 0) *n_items = total;
+    if (e < E) first_item[e] = first;
+    if (e < 16) unit_ctr[e] = 0;   // the wide kernels' per-XCD unit counters
+    if (e == 0) {
+        *n_items = total;
+        first_item[E] = total;
+    }
 }
 
 // ---------------------------------------------------------------- MFMA
@@ -128,23 +135,27 @@ struct GemmParams {
     int H, F;
     void* out;
     bool out_bf16;             // G2 only
+    // wide path: per expert (E + 1 entries) the index of its first item and
+    // its first row; the experts' units are taken in that order
+    const int* first_item;
+    const int32_t* offsets;
+    int E;
+    int* unit_ctr;             // wide path: 8 unit counters, one per XCD, zero at launch
 };
 
 template <int V> struct IC { static constexpr int value = V; };
 
 // GEMM1 epilogue of 4 a-columns [f, f+4) of one row: lane holds the gate
 // and up accumulators of weight rows f + i (fp8: scaled back to real units).
+// sx, sg, su: the fp8 scales of the token and of the gate / up rows (unused
+// for the other kinds).
 template <int KIND>
-BEAM_DEV void store_swiglu(const GemmParams& p, int e, int f, size_t row, int tok, const f32x4& accg,
-                           const f32x4& accu) {
+BEAM_DEV void store_swiglu_s(const GemmParams& p, int f, size_t row, float sx, float4 sg, float4 su,
+                             const f32x4& accg, const f32x4& accu) {
     float gv[4], uv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) { gv[i] = accg[i]; uv[i] = accu[i]; }
     if constexpr (KIND == W_FP8) {
-        const int nrows_w = 2 * p.F;
-        const float sx = p.act_scale[tok];
-        const float4 sg = *reinterpret_cast<const float4*>(p.wscale + (size_t)e * nrows_w + f);
-        const float4 su = *reinterpret_cast<const float4*>(p.wscale + (size_t)e * nrows_w + p.F + f);
         gv[0] *= sx * sg.x; gv[1] *= sx * sg.y; gv[2] *= sx * sg.z; gv[3] *= sx * sg.w;
         uv[0] *= sx * su.x; uv[1] *= sx * su.y; uv[2] *= sx * su.z; uv[3] *= sx * su.w;
         float4 av;
@@ -158,35 +169,56 @@ BEAM_DEV void store_swiglu(const GemmParams& p, int e, int f, size_t row, int to
                                       silu_f32(gv[2]) * uv[2], silu_f32(gv[3]) * uv[3]);
         *reinterpret_cast<float4*>(static_cast<float*>(p.out) + row * p.F + f) = av;
     } else {
-        uint16_t hb[4];
+        float av[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16(silu_f32(gv[i]) * uv[i]);
+        for (int i = 0; i < 4; ++i) av[i] = silu_f32(gv[i]) * uv[i];
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + row * p.F + f) =
-            make_uint2(hb[0] | (uint32_t(hb[1]) << 16), hb[2] | (uint32_t(hb[3]) << 16));
+            make_uint2(pack_bf16x2(av[0], av[1]), pack_bf16x2(av[2], av[3]));
     }
 }
 
-// GEMM2 epilogue of 4 output columns [o, o+4) of one row.
 template <int KIND>
-BEAM_DEV void store_out(const GemmParams& p, int e, int o, size_t row, const f32x4& acc) {
+BEAM_DEV void store_swiglu(const GemmParams& p, int e, int f, size_t row, int tok, const f32x4& accg,
+                           const f32x4& accu) {
+    float sx = 1.f;
+    float4 sg = make_float4(1.f, 1.f, 1.f, 1.f), su = sg;
+    if constexpr (KIND == W_FP8) {
+        const int nrows_w = 2 * p.F;
+        sx = p.act_scale[tok];
+        sg = *reinterpret_cast<const float4*>(p.wscale + (size_t)e * nrows_w + f);
+        su = *reinterpret_cast<const float4*>(p.wscale + (size_t)e * nrows_w + p.F + f);
+    }
+    store_swiglu_s<KIND>(p, f, row, sx, sg, su, accg, accu);
+}
+
+// GEMM2 epilogue of 4 output columns [o, o+4) of one row; sa, sw: the fp8
+// scales of the row and of the weight rows (unused for the other kinds).
+template <int KIND>
+BEAM_DEV void store_out_s(const GemmParams& p, int o, size_t row, float sa, float4 sw, const f32x4& acc) {
     float v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = acc[i];
     if constexpr (KIND == W_FP8) {
-        const float sa = p.act_scale[row];
-        const float4 sw = *reinterpret_cast<const float4*>(p.wscale + (size_t)e * p.H + o);
         v[0] *= sa * sw.x; v[1] *= sa * sw.y; v[2] *= sa * sw.z; v[3] *= sa * sw.w;
     }
     if (p.out_bf16) {
-        uint16_t hb[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16(v[i]);
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + row * p.H + o) =
-            make_uint2(hb[0] | (uint32_t(hb[1]) << 16), hb[2] | (uint32_t(hb[3]) << 16));
+            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
     } else {
         *reinterpret_cast<float4*>(static_cast<float*>(p.out) + row * p.H + o) =
             make_float4(v[0], v[1], v[2], v[3]);
     }
+}
+
+template <int KIND>
+BEAM_DEV void store_out(const GemmParams& p, int e, int o, size_t row, const f32x4& acc) {
+    float sa = 1.f;
+    float4 sw = make_float4(1.f, 1.f, 1.f, 1.f);
+    if constexpr (KIND == W_FP8) {
+        sa = p.act_scale[row];
+        sw = *reinterpret_cast<const float4*>(p.wscale + (size_t)e * p.H + o);
+    }
+    store_out_s<KIND>(p, o, row, sa, sw, acc);
 }
 
 // Epilogue for one 16-column block: lane holds D[4g+i][r] = weight row
@@ -541,9 +573,49 @@ BEAM_DEV i32x8 pair8(uint4 lo, uint4 hi) {
                                    4, 5, 6, 7);
 }
 
-template <int KIND, bool G1, int NB, bool NT>
-BEAM_DEV void gemm_item_wide(const GemmParams& p, int e, int row0, int rows, int tile,
-                             uint4 (*bs)[kWideRows * 16], uint4* ssc) {
+// One work unit of the wide path: N-tile `tile` of item `row0, rows` of
+// expert e, which has cnt items.
+struct WideUnit {
+    int e, row0, rows, tile, cnt;
+};
+
+// Unit j in expert-major, N-tile, item order from the per-expert tables
+// (first item in tab[0, E], first row in tab[E + 1, 2E + 1]); ecur only
+// moves forward, as a workgroup's units do.
+BEAM_DEV WideUnit wide_unit(const int* tab, int E, int nt, int j, int& ecur) {
+    while (__builtin_amdgcn_readfirstlane(tab[ecur + 1]) * nt <= j) ++ecur;
+    const int e = ecur;
+    const int fi = __builtin_amdgcn_readfirstlane(tab[e]);
+    const int cnt = __builtin_amdgcn_readfirstlane(tab[e + 1]) - fi;
+    const int local = j - fi * nt;
+    const int tile = local / cnt, ii = local - tile * cnt;
+    const int row0 = __builtin_amdgcn_readfirstlane(tab[E + 1 + e]) + ii * kWideRows;
+    const int rows = min(kWideRows, __builtin_amdgcn_readfirstlane(tab[E + 2 + e]) - row0);
+    return {e, row0, rows, tile, cnt};
+}
+
+// Activation rows of the loader role (thread t copies chunk t % 16 of item
+// rows t/16 + 16 i): GEMM1 gathers token rows, GEMM2 reads the item's rows.
+// Padding rows of a partial item load a real row (the item's first): an
+// output row depends only on its own input row, and padding rows are never
+// stored.
+template <bool G1>
+BEAM_DEV void wide_srow(const GemmParams& p, const WideUnit& u, int (&srow)[8]) {
+    const int lr = threadIdx.x >> 4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int rr = lr + 16 * i < u.rows ? lr + 16 * i : 0;
+        srow[i] = G1 ? p.row_token[u.row0 + rr] : u.row0 + rr;
+    }
+}
+
+// `ahead` runs once the first K iteration is staged: loads issued there
+// wait behind no load of this unit, and their results are wanted only at
+// its end (the next unit's rows, and this unit's fp8 scales wsv and asv).
+template <int KIND, bool G1, int NB, bool NT, typename Ahead>
+BEAM_DEV void gemm_item_wide(const GemmParams& p, int e, int row0, int rows, int tile, const int (&srow)[8],
+                             const float& wsv, const float& asv, uint4 (*bs)[kWideRows * 16], uint4* ssc,
+                             float* scl, Ahead&& ahead) {
     constexpr bool MX = KIND == W_MXFP4;
     constexpr int NS = (KIND == W_FP8) ? 2 : 4;   // MFMA steps per 256-byte K iteration
     const int lane = threadIdx.x & 63;
@@ -556,14 +628,15 @@ BEAM_DEV void gemm_item_wide(const GemmParams& p, int e, int row0, int rows, int
 
     // loader role: thread t copies chunk c = t % 16 of rows t/16 + 16 i
     const int lc = threadIdx.x & 15, lr = threadIdx.x >> 4;
-    int srow[NB];
+    int sr[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-        // padding rows of a partial item load a real row (the item's first):
-        // an output row depends only on its own input row, and padding
-        // rows are never stored
-        const int rr = lr + 16 * i < rows ? lr + 16 * i : 0;
-        srow[i] = G1 ? p.row_token[row0 + rr] : row0 + rr;
+        if constexpr (MX) {   // gathered here: fewer registers live across the call
+            const int rr = lr + 16 * i < rows ? lr + 16 * i : 0;
+            sr[i] = G1 ? p.row_token[row0 + rr] : row0 + rr;
+        } else {
+            sr[i] = srow[i];
+        }
     }
     const uint8_t* act = p.act + 16 * lc;
     // MXFP4: the E8M0 codes of the item's activation rows for the whole K
@@ -585,7 +658,7 @@ BEAM_DEV void gemm_item_wide(const GemmParams& p, int e, int row0, int rows, int
     uint4 stage[NB];
     auto gload = [&](int k) {
 #pragma unroll
-        for (int i = 0; i < NB; ++i) stage[i] = ld16(act + (size_t)srow[i] * kbytes + k);
+        for (int i = 0; i < NB; ++i) stage[i] = ld16(act + (size_t)sr[i] * kbytes + k);
     };
     auto swrite = [&](int buf) {
 #pragma unroll
@@ -647,6 +720,7 @@ BEAM_DEV void gemm_item_wide(const GemmParams& p, int e, int row0, int rows, int
     }
     swrite(0);
     __syncthreads();
+    ahead();
     // One straight-line body per LDS buffer, the pair unrolled in the loop
     // (no runtime buffer index).  The NS * NB fragment groups of an iteration run
     // as one sequence with the LDS reads kLook groups ahead of their MFMAs
@@ -735,58 +809,163 @@ BEAM_DEV void gemm_item_wide(const GemmParams& p, int e, int row0, int rows, int
     }
     if (kit < nk) body(IC<0>{}, kit);   // odd K-iteration count: the last one
 
+    // fp8: the scales of the tile's 256 weight rows and of the item's rows,
+    // loaded before the K loop, go through LDS to the lanes that need them
+    if constexpr (KIND == W_FP8) {
+        scl[threadIdx.x] = wsv;
+        if (lc < 8) scl[256 + lr + 16 * lc] = asv;
+        __syncthreads();
+    }
+    // the lane's weight rows a[j] + 4 g as positions among the tile's 256
+    const int wave = threadIdx.x >> 6;
+    int lw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lw[j] = G1 ? (j >= 2 ? 128 : 0) + 32 * wave + 16 * (j & 1) : 64 * wave + 16 * j;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         const int c = nb * 16 + r;
         if (c < rows) {
             const size_t row = (size_t)row0 + c;
+            float sx = 1.f;
+            float4 sw[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sw[j] = make_float4(1.f, 1.f, 1.f, 1.f);
+            if constexpr (KIND == W_FP8) {
+                sx = scl[256 + c];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sw[j] = *reinterpret_cast<const float4*>(scl + lw[j] + 4 * g);
+            }
             if constexpr (G1) {
-                const int tok = p.row_token[row0 + c];
-                store_swiglu<KIND>(p, e, a[0] + 4 * g, row, tok, acc[0][nb], acc[2][nb]);
-                store_swiglu<KIND>(p, e, a[1] + 4 * g, row, tok, acc[1][nb], acc[3][nb]);
+                store_swiglu_s<KIND>(p, a[0] + 4 * g, row, sx, sw[0], sw[2], acc[0][nb], acc[2][nb]);
+                store_swiglu_s<KIND>(p, a[1] + 4 * g, row, sx, sw[1], sw[3], acc[1][nb], acc[3][nb]);
             } else {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) store_out<KIND>(p, e, a[j] + 4 * g, row, acc[j][nb]);
+                for (int j = 0; j < 4; ++j) store_out_s<KIND>(p, a[j] + 4 * g, row, sx, sw[j], acc[j][nb]);
             }
         }
     }
 }
 
-template <int KIND, bool G1, bool NT>
-BEAM_DEV void dispatch_wide(const GemmParams& p, int4 it, int tile, uint4 (*bs)[kWideRows * 16], uint4* ssc) {
-    if (it.z <= 32)
-        gemm_item_wide<KIND, G1, 2, NT>(p, it.x, it.y, it.z, tile, bs, ssc);
-    else if (it.z <= 64)
-        gemm_item_wide<KIND, G1, 4, NT>(p, it.x, it.y, it.z, tile, bs, ssc);
+template <int KIND, bool G1, bool NT, typename Ahead>
+BEAM_DEV void dispatch_wide(const GemmParams& p, const WideUnit& u, const int (&srow)[8], const float& wsv,
+                            const float& asv, uint4 (*bs)[kWideRows * 16], uint4* ssc, float* scl, Ahead&& ahead) {
+    if (u.rows <= 32)
+        gemm_item_wide<KIND, G1, 2, NT>(p, u.e, u.row0, u.rows, u.tile, srow, wsv, asv, bs, ssc, scl, ahead);
+    else if (u.rows <= 64)
+        gemm_item_wide<KIND, G1, 4, NT>(p, u.e, u.row0, u.rows, u.tile, srow, wsv, asv, bs, ssc, scl, ahead);
     else
-        gemm_item_wide<KIND, G1, 8, NT>(p, it.x, it.y, it.z, tile, bs, ssc);
+        gemm_item_wide<KIND, G1, 8, NT>(p, u.e, u.row0, u.rows, u.tile, srow, wsv, asv, bs, ssc, scl, ahead);
 }
 
-// Block -> (item, N-tile).  Work units are ordered expert by expert, N-tile
-// by N-tile, item by item, so the items of one expert that share an N-tile
-// of weights are neighbours.  Workgroups go to the 8 XCDs round-robin
-// (block b runs on XCD b % 8), so each XCD is given one contiguous range of
-// units: neighbours share its L2 and each weight tile is fetched once for
-// all the items of its expert.
+// Persistent: one workgroup per CU.  Work units are ordered expert by
+// expert, N-tile by N-tile, item by item, so the items of one expert that
+// share an N-tile of weights are neighbours.  Workgroups go to the 8 XCDs
+// round-robin (block b runs on XCD b % 8), so each XCD is given one
+// contiguous range of units, which its workgroups take in order from a
+// counter of their own: neighbours run together, share the XCD's L2, and
+// each weight tile is fetched about once for all the items of its expert;
+// a workgroup that draws short units draws more of them.  A unit's position
+// is computed from two per-expert tables held in LDS, and the gather
+// indices of the next unit (and the fp8 scales of this one) are loaded
+// before the K loop, so a unit starts with a single round trip to memory.
+// Every unit is computed whole by one workgroup, so the result does not
+// depend on which workgroup takes it.
 template <int KIND, bool G1>
 __global__ __launch_bounds__(256, 1) void beam_expert_gemm_wide(GemmParams p) {
     __shared__ uint4 bs[2][kWideRows * 16];
     // MXFP4: the activation rows' E8M0 codes for the whole K (16 per K iteration)
     __shared__ uint4 ssc[KIND == W_MXFP4 ? kWideRows * 16 : 1];
-    const int total = *p.n_items * p.n_tiles;
+    // fp8: scales of the tile's 256 weight rows, then of the item's 128 rows
+    __shared__ __align__(16) float scl[KIND == W_FP8 ? 384 : 4];
+    __shared__ int tab[2 * (kMaxExperts + 1)];
+    __shared__ int nxt[2];
+    const int E = p.E, nt = p.n_tiles;
+    if constexpr (KIND == W_MXFP4) {
+        // no registers to spare for a unit loop: one unit per workgroup, and
+        // the item gathers its own rows
+        const int total = *p.n_items * nt;
+        const int per_xcd = (total + 7) >> 3;
+        const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+        if (slot >= per_xcd) return;
+        const int j = xcd * per_xcd + slot;
+        if (j >= total) return;
+        const int4 any = p.items[j / nt];             // an item of the unit's expert
+        const int cnt = any.w & 0xFFFF;
+        const int first = j / nt - (any.w >> 16);     // the expert's first item
+        const int local = j - first * nt;             // = tile * cnt + item within the expert
+        const int tile = local / cnt;
+        const int4 it = p.items[first + (local - tile * cnt)];
+        const WideUnit u{it.x, it.y, it.z, tile, cnt};
+        const int srow[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        const float one = 1.f;
+        auto none = [] {};
+        if (cnt == 1) dispatch_wide<KIND, G1, true>(p, u, srow, one, one, bs, ssc, scl, none);
+        else dispatch_wide<KIND, G1, false>(p, u, srow, one, one, bs, ssc, scl, none);
+        return;
+    }
+    for (int i = threadIdx.x; i <= E; i += 256) {
+        tab[i] = p.first_item[i];
+        tab[E + 1 + i] = p.offsets[i];
+    }
+    __syncthreads();
+    const int total = __builtin_amdgcn_readfirstlane(tab[E]) * nt;
     const int per_xcd = (total + 7) >> 3;
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    if (slot >= per_xcd) return;
-    const int j = xcd * per_xcd + slot;
-    if (j >= total) return;
-    const int4 any = p.items[j / p.n_tiles];          // an item of the unit's expert
-    const int cnt = any.w & 0xFFFF;
-    const int first = j / p.n_tiles - (any.w >> 16);  // the expert's first item
-    const int local = j - first * p.n_tiles;          // = tile * cnt + item within the expert
-    const int tile = local / cnt;
-    const int4 it = p.items[first + (local - tile * cnt)];
-    if (cnt == 1) dispatch_wide<KIND, G1, true>(p, it, tile, bs, ssc);
-    else dispatch_wide<KIND, G1, false>(p, it, tile, bs, ssc);
+    const int xcd = blockIdx.x & 7;
+    const int base = xcd * per_xcd, end = min(total, base + per_xcd);
+    // the XCD's units are handed out in order by its counter; a workgroup
+    // holds the index of its next unit while it runs one, and asks for the
+    // one after while the next one's rows are being gathered
+    int* ctr = p.unit_ctr + xcd;
+    if (threadIdx.x == 0) {
+        nxt[0] = atomicAdd(ctr, 1);
+        nxt[1] = atomicAdd(ctr, 1);
+    }
+    __syncthreads();
+    int j = base + nxt[0], jn = base + nxt[1];
+    if (j >= end) return;
+    const int lc = threadIdx.x & 15;
+    int ecur = 0;
+    WideUnit u = wide_unit(tab, E, nt, j, ecur);
+    int srow[8];
+    wide_srow<G1>(p, u, srow);
+    for (;;) {
+        const bool more = jn < end;
+        int fut = 0;
+        WideUnit un = u;
+        int srown[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        float wsv = 1.f, asv = 1.f;
+        auto ahead = [&] {
+            if (more) {
+                if (threadIdx.x == 0) fut = atomicAdd(ctr, 1);
+                un = wide_unit(tab, E, nt, jn, ecur);
+                wide_srow<G1>(p, un, srown);
+            }
+            if constexpr (KIND == W_FP8) {
+                const int t = threadIdx.x;
+                const size_t wr = G1 ? (size_t)u.e * 2 * p.F + (t < 128 ? 0 : p.F) + u.tile * 128 + (t & 127)
+                                     : (size_t)u.e * p.H + u.tile * 256 + t;
+                wsv = p.wscale[wr];
+                int sr = srow[0];
+#pragma unroll
+                for (int i = 1; i < 8; ++i) sr = (lc & 7) == i ? srow[i] : sr;
+                if (lc < 8) asv = p.act_scale[sr];
+            }
+        };
+        // weights read once (single-item expert): non-temporal; shared by the
+        // expert's other items: plain loads that stay in L2
+        if (u.cnt == 1) dispatch_wide<KIND, G1, true>(p, u, srow, wsv, asv, bs, ssc, scl, ahead);
+        else dispatch_wide<KIND, G1, false>(p, u, srow, wsv, asv, bs, ssc, scl, ahead);
+        if (!more) break;
+        // nxt was last read before this unit's K loop, whose barriers every
+        // wave has passed since
+        if (threadIdx.x == 0) nxt[0] = fut;
+        __syncthreads();
+        j = jn;
+        jn = base + nxt[0];
+        u = un;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) srow[i] = srown[i];
+    }
 }
 
 // Per-row e4m3 re-quantisation of the fp32 SwiGLU output (fp8 path): one
@@ -820,8 +999,8 @@ __global__ __launch_bounds__(256) void beam_swiglu_slices(const float* __restric
         gs.x += gv.x; gs.y += gv.y; gs.z += gv.z; gs.w += gv.w;
         vs.x += uv.x; vs.y += uv.y; vs.z += uv.z; vs.w += uv.w;
     }
-    const uint32_t lo = f32_to_bf16(silu_f32(gs.x) * vs.x) | (uint32_t(f32_to_bf16(silu_f32(gs.y) * vs.y)) << 16);
-    const uint32_t hi = f32_to_bf16(silu_f32(gs.z) * vs.z) | (uint32_t(f32_to_bf16(silu_f32(gs.w) * vs.w)) << 16);
+    const uint32_t lo = pack_bf16x2(silu_f32(gs.x) * vs.x, silu_f32(gs.y) * vs.y);
+    const uint32_t hi = pack_bf16x2(silu_f32(gs.z) * vs.z, silu_f32(gs.w) * vs.w);
     *reinterpret_cast<uint2*>(a + i) = make_uint2(lo, hi);
 }
 
@@ -885,10 +1064,10 @@ static size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 //   < 256:     mostly one 128-row item per expert, so each weight byte is
 //              streamed once: two 16-row weight tiles per wave, two waves
 //              per SIMD for more bytes in flight (beam_expert_gemm_lds);
-//   >= 256:    256-row items, several per expert, sharing each weight tile
+//   >= 256:    128-row items, several per expert, sharing each weight tile
 //              through L2: four weight tiles per wave, XCD-grouped work
-//              order (beam_expert_gemm_wide), grid rounded to whole XCD
-//              rounds.
+//              order, one persistent workgroup per CU
+//              (beam_expert_gemm_wide).
 enum GemmPath { PATH_DIRECT, PATH_LDS, PATH_WIDE };
 
 static GemmPath gemm_path(int T, int K, int E) {
@@ -911,6 +1090,8 @@ static size_t max_items(int T, int K, int E) {
 
 struct ExpertsWs {
     int* n_items;
+    int* unit_ctr;     // 16 counters: GEMM1's 8, then GEMM2's
+    int* first_item;   // [E + 1]: first item of each expert, then the item count
     int4* items;
     void* a;        // bf16 [TK,F] (BF16) or fp32 [TK,F] (FP8, MXFP4, F32)
     uint8_t* aq;    // FP8: e4m3 [TK,F]; MXFP4: packed E2M1 [TK,F/2]
@@ -925,7 +1106,10 @@ static ExpertsWs carve(void* base, int T, int K, int E, int F, WKind w) {
     uint8_t* p = static_cast<uint8_t*>(base);
     size_t off = 0;
     s.n_items = reinterpret_cast<int*>(p + off);
+    s.unit_ctr = s.n_items + 16;
     off += 256;
+    s.first_item = reinterpret_cast<int*>(p + off);
+    off += align256((size_t)(E + 1) * sizeof(int));
     s.items = reinterpret_cast<int4*>(p + off);
     off += align256(max_items(T, K, E) * sizeof(int4));
     s.a = p + off;
@@ -952,13 +1136,29 @@ size_t experts_ws_bytes(int T, int K, int E, int H, int F, WKind w) {
 }
 
 
+// compute units of the current device (looked up once per device)
+static int device_cus() {
+    static int cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
 template <int KIND, bool G1>
 static void launch_gemm(GemmParams p, int n_items_max, GemmPath path, hipStream_t st) {
     const int H = p.H, F = p.F;
     if (path == PATH_WIDE) {
         p.n_tiles = G1 ? F / 128 : H / 256;
-        const int blocks = (n_items_max * p.n_tiles + 7) / 8 * 8;
-        hipLaunchKernelGGL((beam_expert_gemm_wide<KIND, G1>), dim3(blocks), dim3(256), 0, st, p);
+        // one workgroup per CU, the same number on each XCD (MXFP4: one
+        // workgroup per unit)
+        const int per_xcd = (n_items_max * p.n_tiles + 7) / 8;
+        const int slots = KIND == W_MXFP4 ? per_xcd : std::max(1, std::min(per_xcd, device_cus() / 8));
+        hipLaunchKernelGGL((beam_expert_gemm_wide<KIND, G1>), dim3(8 * slots), dim3(256), 0, st, p);
         return;
     }
     p.n_tiles = G1 ? F / 64 : H / 128;
@@ -983,11 +1183,15 @@ hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st) {
     const int n_items_max = (int)max_items(a.T, a.K, a.E);
     const GemmPath path = gemm_path(a.T, a.K, a.E);
     hipLaunchKernelGGL(beam_build_items, dim3(1), dim3(256), 0, st, a.offsets, a.E, mc, ws.items,
-                       ws.n_items);
+                       ws.n_items, ws.first_item, ws.unit_ctr);
 
     GemmParams p{};
     p.items = ws.items;
     p.n_items = ws.n_items;
+    p.first_item = ws.first_item;
+    p.offsets = a.offsets;
+    p.E = a.E;
+    p.unit_ctr = ws.unit_ctr;
     p.H = a.H;
     p.F = a.F;
     p.ksplit = 1;
@@ -1028,6 +1232,7 @@ hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st) {
         p.out_slice = a.y_slice_stride;
     }
     p.row_token = nullptr;
+    p.unit_ctr = ws.unit_ctr + 8;
     p.W = static_cast<const uint8_t*>(a.wd);
     p.wscale = static_cast<const float*>(a.sd);
     p.out = a.y;

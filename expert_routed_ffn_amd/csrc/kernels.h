@@ -43,6 +43,9 @@ hipError_t launch_quantize_x_e4m3(const uint16_t* x, int T, int H, uint8_t* xq, 
 
 enum WKind { W_F32 = 0, W_BF16 = 1, W_FP8 = 2, W_MXFP4 = 3 };
 
+// most experts per layer (the item builder gives each expert one thread)
+constexpr int kMaxExperts = 256;
+
 struct ExpertsArgs {
     int T, K, E, H, F;
     WKind w;
