@@ -610,12 +610,13 @@ BEAM_DEV void wide_srow(const GemmParams& p, const WideUnit& u, int (&srow)[8]) 
 }
 
 // `ahead` runs once the first K iteration is staged: loads issued there
-// wait behind no load of this unit, and their results are wanted only at
-// its end (the next unit's rows, and this unit's fp8 scales wsv and asv).
-template <int KIND, bool G1, int NB, bool NT, typename Ahead>
+// wait behind no load of this unit, and their results (this unit's fp8
+// scales wsv and asv) are wanted only at its end.  `tail` runs after the
+// last MFMA is issued, before the epilogue.
+template <int KIND, bool G1, int NB, bool NT, typename Ahead, typename Tail>
 BEAM_DEV void gemm_item_wide(const GemmParams& p, int e, int row0, int rows, int tile, const int (&srow)[8],
                              const float& wsv, const float& asv, uint4 (*bs)[kWideRows * 16], uint4* ssc,
-                             float* scl, Ahead&& ahead) {
+                             float* scl, Ahead&& ahead, Tail&& tail) {
     constexpr bool MX = KIND == W_MXFP4;
     constexpr int NS = (KIND == W_FP8) ? 2 : 4;   // MFMA steps per 256-byte K iteration
     const int lane = threadIdx.x & 63;
@@ -808,6 +809,7 @@ BEAM_DEV void gemm_item_wide(const GemmParams& p, int e, int row0, int rows, int
         body(IC<1>{}, kit + 1);
     }
     if (kit < nk) body(IC<0>{}, kit);   // odd K-iteration count: the last one
+    tail();
 
     // fp8: the scales of the tile's 256 weight rows and of the item's rows,
     // loaded before the K loop, go through LDS to the lanes that need them
@@ -846,15 +848,16 @@ BEAM_DEV void gemm_item_wide(const GemmParams& p, int e, int row0, int rows, int
     }
 }
 
-template <int KIND, bool G1, bool NT, typename Ahead>
+template <int KIND, bool G1, bool NT, typename Ahead, typename Tail>
 BEAM_DEV void dispatch_wide(const GemmParams& p, const WideUnit& u, const int (&srow)[8], const float& wsv,
-                            const float& asv, uint4 (*bs)[kWideRows * 16], uint4* ssc, float* scl, Ahead&& ahead) {
+                            const float& asv, uint4 (*bs)[kWideRows * 16], uint4* ssc, float* scl, Ahead&& ahead,
+                            Tail&& tail) {
     if (u.rows <= 32)
-        gemm_item_wide<KIND, G1, 2, NT>(p, u.e, u.row0, u.rows, u.tile, srow, wsv, asv, bs, ssc, scl, ahead);
+        gemm_item_wide<KIND, G1, 2, NT>(p, u.e, u.row0, u.rows, u.tile, srow, wsv, asv, bs, ssc, scl, ahead, tail);
     else if (u.rows <= 64)
-        gemm_item_wide<KIND, G1, 4, NT>(p, u.e, u.row0, u.rows, u.tile, srow, wsv, asv, bs, ssc, scl, ahead);
+        gemm_item_wide<KIND, G1, 4, NT>(p, u.e, u.row0, u.rows, u.tile, srow, wsv, asv, bs, ssc, scl, ahead, tail);
     else
-        gemm_item_wide<KIND, G1, 8, NT>(p, u.e, u.row0, u.rows, u.tile, srow, wsv, asv, bs, ssc, scl, ahead);
+        gemm_item_wide<KIND, G1, 8, NT>(p, u.e, u.row0, u.rows, u.tile, srow, wsv, asv, bs, ssc, scl, ahead, tail);
 }
 
 // Persistent: one workgroup per CU.  Work units are ordered expert by
@@ -865,9 +868,8 @@ BEAM_DEV void dispatch_wide(const GemmParams& p, const WideUnit& u, const int (&
 // counter of their own: neighbours run together, share the XCD's L2, and
 // each weight tile is fetched about once for all the items of its expert;
 // a workgroup that draws short units draws more of them.  A unit's position
-// is computed from two per-expert tables held in LDS, and the gather
-// indices of the next unit (and the fp8 scales of this one) are loaded
-// before the K loop, so a unit starts with a single round trip to memory.
+// is computed from two per-expert tables held in LDS (no memory round
+// trip), and its fp8 epilogue scales are loaded behind its first K stage.
 // Every unit is computed whole by one workgroup, so the result does not
 // depend on which workgroup takes it.
 template <int KIND, bool G1>
@@ -878,7 +880,7 @@ __global__ __launch_bounds__(256, 1) void beam_expert_gemm_wide(GemmParams p) {
     // fp8: scales of the tile's 256 weight rows, then of the item's 128 rows
     __shared__ __align__(16) float scl[KIND == W_FP8 ? 384 : 4];
     __shared__ int tab[2 * (kMaxExperts + 1)];
-    __shared__ int nxt[2];
+    __shared__ int nxt[1];
     const int E = p.E, nt = p.n_tiles;
     if constexpr (KIND == W_MXFP4) {
         // no registers to spare for a unit loop: one unit per workgroup, and
@@ -899,8 +901,8 @@ __global__ __launch_bounds__(256, 1) void beam_expert_gemm_wide(GemmParams p) {
         const int srow[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         const float one = 1.f;
         auto none = [] {};
-        if (cnt == 1) dispatch_wide<KIND, G1, true>(p, u, srow, one, one, bs, ssc, scl, none);
-        else dispatch_wide<KIND, G1, false>(p, u, srow, one, one, bs, ssc, scl, none);
+        if (cnt == 1) dispatch_wide<KIND, G1, true>(p, u, srow, one, one, bs, ssc, scl, none, none);
+        else dispatch_wide<KIND, G1, false>(p, u, srow, one, one, bs, ssc, scl, none, none);
         return;
     }
     for (int i = threadIdx.x; i <= E; i += 256) {
@@ -913,15 +915,13 @@ __global__ __launch_bounds__(256, 1) void beam_expert_gemm_wide(GemmParams p) {
     const int xcd = blockIdx.x & 7;
     const int base = xcd * per_xcd, end = min(total, base + per_xcd);
     // the XCD's units are handed out in order by its counter; a workgroup
-    // holds the index of its next unit while it runs one, and asks for the
-    // one after while the next one's rows are being gathered
+    // asks for its next unit when its last MFMA of this one has issued, so
+    // the answer comes back during the epilogue, and the units running on
+    // the XCD stay neighbours
     int* ctr = p.unit_ctr + xcd;
-    if (threadIdx.x == 0) {
-        nxt[0] = atomicAdd(ctr, 1);
-        nxt[1] = atomicAdd(ctr, 1);
-    }
+    if (threadIdx.x == 0) nxt[0] = atomicAdd(ctr, 1);
     __syncthreads();
-    int j = base + nxt[0], jn = base + nxt[1];
+    int j = base + nxt[0];
     if (j >= end) return;
     const int lc = threadIdx.x & 15;
     int ecur = 0;
@@ -929,17 +929,9 @@ __global__ __launch_bounds__(256, 1) void beam_expert_gemm_wide(GemmParams p) {
     int srow[8];
     wide_srow<G1>(p, u, srow);
     for (;;) {
-        const bool more = jn < end;
         int fut = 0;
-        WideUnit un = u;
-        int srown[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         float wsv = 1.f, asv = 1.f;
         auto ahead = [&] {
-            if (more) {
-                if (threadIdx.x == 0) fut = atomicAdd(ctr, 1);
-                un = wide_unit(tab, E, nt, jn, ecur);
-                wide_srow<G1>(p, un, srown);
-            }
             if constexpr (KIND == W_FP8) {
                 const int t = threadIdx.x;
                 const size_t wr = G1 ? (size_t)u.e * 2 * p.F + (t < 128 ? 0 : p.F) + u.tile * 128 + (t & 127)
@@ -951,20 +943,21 @@ __global__ __launch_bounds__(256, 1) void beam_expert_gemm_wide(GemmParams p) {
                 if (lc < 8) asv = p.act_scale[sr];
             }
         };
+        auto tail = [&] {
+            if (threadIdx.x == 0) fut = atomicAdd(ctr, 1);
+        };
         // weights read once (single-item expert): non-temporal; shared by the
         // expert's other items: plain loads that stay in L2
-        if (u.cnt == 1) dispatch_wide<KIND, G1, true>(p, u, srow, wsv, asv, bs, ssc, scl, ahead);
-        else dispatch_wide<KIND, G1, false>(p, u, srow, wsv, asv, bs, ssc, scl, ahead);
-        if (!more) break;
+        if (u.cnt == 1) dispatch_wide<KIND, G1, true>(p, u, srow, wsv, asv, bs, ssc, scl, ahead, tail);
+        else dispatch_wide<KIND, G1, false>(p, u, srow, wsv, asv, bs, ssc, scl, ahead, tail);
         // nxt was last read before this unit's K loop, whose barriers every
         // wave has passed since
         if (threadIdx.x == 0) nxt[0] = fut;
         __syncthreads();
-        j = jn;
-        jn = base + nxt[0];
-        u = un;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) srow[i] = srown[i];
+        j = base + nxt[0];
+        if (j >= end) break;
+        u = wide_unit(tab, E, nt, j, ecur);
+        wide_srow<G1>(p, u, srow);
     }
 }
 
