@@ -355,6 +355,10 @@ BEAM_DEV void gemm_item_direct(const GemmParams& p, int e, int row0, int rows, i
 // shared by the 4 waves; weights keep streaming into registers.
 constexpr int kLdsRows = 128;
 constexpr int kWideRows = 128;   // rows of a work item on the wide path
+// rows of a 4-bit work item on the LDS path: eight 16-row blocks of E2M1
+// operands (each MFMA takes them zero-padded to eight registers) do not fit
+// in the registers of one wave
+constexpr int kLdsRowsMx = 64;
 constexpr int kLook = 3;         // wide path: LDS fragment reads issued this many groups ahead
 
 // LDS position of 16-byte chunk c of staged row rr: chunks are XOR-swizzled
@@ -520,9 +524,9 @@ BEAM_DEV void dispatch_lds(const GemmParams& p, int4 it, int tile, uint4 (*bs)[k
         gemm_item_lds<KIND, G1, 1, NT>(p, it.x, it.y, it.z, tile, bs, bss);
     else if (it.z <= 32)
         gemm_item_lds<KIND, G1, 2, NT>(p, it.x, it.y, it.z, tile, bs, bss);
-    else if (it.z <= 64)
+    else if (KIND == W_MXFP4 || it.z <= 64)   // 4-bit items hold at most kLdsRowsMx rows
         gemm_item_lds<KIND, G1, 4, NT>(p, it.x, it.y, it.z, tile, bs, bss);
-    else
+    else if constexpr (KIND != W_MXFP4)
         gemm_item_lds<KIND, G1, 8, NT>(p, it.x, it.y, it.z, tile, bs, bss);
 }
 
@@ -1068,17 +1072,17 @@ static GemmPath gemm_path(int T, int K, int E) {
     return (long long)T * K >= 256LL * E ? PATH_WIDE : PATH_LDS;
 }
 
-static int rows_per_item(int T, int K, int E) {
+static int rows_per_item(int T, int K, int E, WKind w) {
     switch (gemm_path(T, K, E)) {
         case PATH_DIRECT: return 16;
-        case PATH_LDS: return kLdsRows;
+        case PATH_LDS: return w == W_MXFP4 ? kLdsRowsMx : kLdsRows;
         default: return kWideRows;
     }
 }
 
-static size_t max_items(int T, int K, int E) {
+static size_t max_items(int T, int K, int E, WKind w) {
     const size_t TK = (size_t)T * K;
-    return TK / rows_per_item(T, K, E) + (size_t)std::min<size_t>(E, TK);
+    return TK / rows_per_item(T, K, E, w) + (size_t)std::min<size_t>(E, TK);
 }
 
 struct ExpertsWs {
@@ -1104,7 +1108,7 @@ static ExpertsWs carve(void* base, int T, int K, int E, int F, WKind w) {
     s.first_item = reinterpret_cast<int*>(p + off);
     off += align256((size_t)(E + 1) * sizeof(int));
     s.items = reinterpret_cast<int4*>(p + off);
-    off += align256(max_items(T, K, E) * sizeof(int4));
+    off += align256(max_items(T, K, E, w) * sizeof(int4));
     s.a = p + off;
     off += align256(TK * F * (w == W_BF16 ? 2 : 4));
     if (w == W_FP8) {
@@ -1172,8 +1176,8 @@ hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st) {
                            a.offsets, (const float*)a.wd, a.E, a.H, a.F, a.y, a.y_bf16);
         return hipGetLastError();
     }
-    const int mc = rows_per_item(a.T, a.K, a.E);
-    const int n_items_max = (int)max_items(a.T, a.K, a.E);
+    const int mc = rows_per_item(a.T, a.K, a.E, a.w);
+    const int n_items_max = (int)max_items(a.T, a.K, a.E, a.w);
     const GemmPath path = gemm_path(a.T, a.K, a.E);
     hipLaunchKernelGGL(beam_build_items, dim3(1), dim3(256), 0, st, a.offsets, a.E, mc, ws.items,
                        ws.n_items, ws.first_item, ws.unit_ctr);
