@@ -76,7 +76,44 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=8)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device copies of MIB MiB (counter calibration) and exit")
+    ap.add_argument("--gemm-reference", action="store_true",
+                    help="only time the vendor library (hipBLASLt through torch) on dense bf16 / fp8 GEMMs "
+                         "of the expert GEMM sizes, as a reference for the expert kernels, and exit")
     return ap.parse_args()
+
+
+def gemm_reference():
+    """Dense GEMMs in the vendor library at the expert GEMM sizes, one JSON
+    line each: all T*K = 131072 rows of the T = 16384 layer against one
+    weight matrix (GEMM1 5120 x 5120, GEMM2 5120 x 2560), and one expert's
+    share (512 rows).  A reference for the grouped kernels, not a path of
+    the layer."""
+    import torch
+    dev = "cuda:0"
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, n=10):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(n):
+            fn()
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / n * 1e3
+
+    for M, N, K in [(131072, 5120, 5120), (131072, 5120, 2560), (512, 5120, 5120), (512, 5120, 2560)]:
+        a = torch.randn(M, K, device=dev, dtype=torch.bfloat16)
+        b = torch.randn(N, K, device=dev, dtype=torch.bfloat16)
+        flop = 2.0 * M * N * K
+        us = timed(lambda: a @ b.t())
+        a8, b8 = a.to(torch.float8_e4m3fn), b.to(torch.float8_e4m3fn)
+        one = torch.ones((), device=dev)
+        us8 = timed(lambda: torch._scaled_mm(a8, b8.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16))
+        print(json.dumps({"gemm": [M, N, K], "bf16_us": round(us, 1), "bf16_tflops": round(flop / us / 1e6, 1),
+                          "fp8_us": round(us8, 1), "fp8_tflops": round(flop / us8 / 1e6, 1)}), flush=True)
+        del a, b, a8, b8
 
 
 class HipEvents:
@@ -508,6 +545,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "copies": 3}))
+        return
+    if args.gemm_reference:
+        gemm_reference()
         return
     import expert_routed_ffn_amd as beam
     import synth
