@@ -508,13 +508,60 @@ BEAM_DEV void gemm_item_lds(const GemmParams& p, int e, int row0, int rows, int 
     }
 }
 
+// Item i of the direct path: the i-th expert, in expert order, that has
+// rows (at T <= 16 an expert has at most T rows, so each touched expert is
+// one item).  Every wave finds it in the offsets on its own, lane l looking
+// at experts 4l .. 4l+3 (E <= 256), with one round trip to memory and no
+// item list.  Returns false past the last touched expert.
+BEAM_DEV bool direct_item(const int32_t* __restrict__ off, int E, int i, int& e, int& row0, int& rows) {
+    const int lane = threadIdx.x & 63;
+    int o[5];
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+        const int x = 4 * lane + j;
+        o[j] = off[x <= E ? x : E];
+    }
+    bool f[4];
+    int before = 0, mine = 0, total = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f[j] = 4 * lane + j < E && o[j + 1] > o[j];
+        const unsigned long long b = __ballot(f[j]);
+        // touched experts 4m + j of the lanes m below this one
+        before += __builtin_amdgcn_mbcnt_hi((unsigned)(b >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)b, 0));
+        mine += f[j] ? 1 : 0;
+        total += __popcll(b);
+    }
+    if (i >= total) return false;
+    // experts below 4l + j, in order: those of the lanes below (before) and
+    // this lane's set flags j' < j
+    int jj = 0, seen = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (f[j] && before + seen == i) jj = j;
+        seen += f[j] ? 1 : 0;
+    }
+    const unsigned long long owner = __ballot(before <= i && i < before + mine);
+    const int L = __ffsll(owner) - 1;   // the one lane holding expert number i
+    int lo = o[0], hi = o[1];
+#pragma unroll
+    for (int j = 1; j < 4; ++j) {
+        lo = jj == j ? o[j] : lo;
+        hi = jj == j ? o[j + 1] : hi;
+    }
+    e = __builtin_amdgcn_readlane(4 * lane + jj, L);
+    row0 = __builtin_amdgcn_readlane(lo, L);
+    rows = __builtin_amdgcn_readlane(hi, L) - row0;
+    return true;
+}
+
 template <int KIND, bool G1>
 __global__ __launch_bounds__(256) void beam_expert_gemm_direct(GemmParams p) {
     const int item = blockIdx.x / p.n_tiles;
     const int tile = blockIdx.x - item * p.n_tiles;
-    if (item >= *p.n_items) return;
-    const int4 it = p.items[item];
-    gemm_item_direct<KIND, G1>(p, it.x, it.y, it.z, tile);
+    int e, row0, rows;
+    if (!direct_item(p.offsets, p.E, item, e, row0, rows)) return;
+    gemm_item_direct<KIND, G1>(p, e, row0, rows, tile);
 }
 
 template <int KIND, bool G1, bool NT>
@@ -1179,8 +1226,10 @@ hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st) {
     const int mc = rows_per_item(a.T, a.K, a.E, a.w);
     const int n_items_max = (int)max_items(a.T, a.K, a.E, a.w);
     const GemmPath path = gemm_path(a.T, a.K, a.E);
-    hipLaunchKernelGGL(beam_build_items, dim3(1), dim3(256), 0, st, a.offsets, a.E, mc, ws.items,
-                       ws.n_items, ws.first_item, ws.unit_ctr);
+    // the direct kernels find their items in the offsets themselves
+    if (path != PATH_DIRECT)
+        hipLaunchKernelGGL(beam_build_items, dim3(1), dim3(256), 0, st, a.offsets, a.E, mc, ws.items,
+                           ws.n_items, ws.first_item, ws.unit_ctr);
 
     GemmParams p{};
     p.items = ws.items;
