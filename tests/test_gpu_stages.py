@@ -289,6 +289,29 @@ def test_experts_every_token_on_one_expert():
     check_output("y", got, ref, "bf16")
 
 
+@pytest.mark.parametrize("w_dtype,E,G,T,case", [
+    ("bf16", 6, 3, 5, "ends"),      # E not a multiple of 4 (a lane's last experts are past E)
+    ("bf16", 6, 3, 16, "one"),      # every token on the last expert: one 16-row item
+    ("fp8", 12, 3, 9, "ends"),
+    ("mxfp4", 6, 3, 3, "ends"),
+])
+def test_experts_direct_items(w_dtype, E, G, T, case):
+    # At T <= 16 each wave finds its item (the i-th touched expert) in the
+    # offsets; cover the first and last expert, untouched experts between,
+    # and expert counts that do not fill a lane's four slots
+    say(f"experts direct items {w_dtype} E={E} T={T} {case}")
+    K = 2
+    wl = synth.Workload("stage", T=1, hidden=512, n_experts=E, n_groups=G, topk_groups=G, topk=K,
+                        group_topn=1, d_ff=512 if w_dtype == "mxfp4" else 256, routed_scale=2.5, rms_eps=1e-6,
+                        n=20, act_dtype="bf16", w_dtype=w_dtype, bias_sigma=0.02, seed=11)
+    if case == "ends":
+        ids = np.array([[0, E - 1] if t % 2 == 0 else [E - 1, 1 + t % (E - 2)] for t in range(T)])
+    else:
+        ids = np.array([[E - 1, t % (E - 1)] for t in range(T)])
+    got, ref = _run_experts_stage(wl, T, ids, torch.float32)
+    check_output("y", got, ref, {"bf16": "bf16", "fp8": "fp8", "mxfp4": "mx"}[w_dtype])
+
+
 def test_experts_beam_shape_few_tokens():
     say("experts: Beam shape, bf16, T=3")
     wl = synth.WORKLOADS["decode_t8"]
