@@ -17,14 +17,21 @@ namespace beam {
 constexpr int kMaxIt = 8;    // chunks of 4 per thread: H <= 8 * 1024
 constexpr int kSmallT = 256; // up to this many tokens the grid is too small to hide latency
 
-// 4 consecutive elements as fp32
-template <bool BF> BEAM_DEV float4 ld4(const void* p, size_t i) {
+// 4 consecutive elements as fp32; NT: a streaming (non-temporal) load, for
+// data this kernel reads once (the expert rows y, the token's h), which
+// should not push the reused gammas out of the caches
+template <bool BF, bool NT = false> BEAM_DEV float4 ld4(const void* p, size_t i) {
     if constexpr (BF) {
-        const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+        typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
+        const u32x2v* q = reinterpret_cast<const u32x2v*>(static_cast<const uint16_t*>(p) + i);
+        const u32x2v u = NT ? __builtin_nontemporal_load(q) : *q;
         return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
                            __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
     } else {
-        return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+        typedef float f32x4v __attribute__((ext_vector_type(4)));
+        const f32x4v* q = reinterpret_cast<const f32x4v*>(static_cast<const float*>(p) + i);
+        const f32x4v v = NT ? __builtin_nontemporal_load(q) : *q;
+        return make_float4(v.x, v.y, v.z, v.w);
     }
 }
 template <bool BF> BEAM_DEV float rnd_act(float v) {
@@ -73,7 +80,7 @@ __global__ __launch_bounds__(256) void beam_combine_norm(CombineArgs a) {
             for (int it = 0; it < NIT; ++it) {
                 const int i = (it * 256 + tid) * 4;
                 if (i < H) {
-                    hv[it] = ld4<ABF>(a.h, rowo + i);
+                    hv[it] = ld4<ABF, true>(a.h, rowo + i);
                     gpo[it] = ld4<ABF>(a.gpost, i);
                     gpr[it] = ld4<ABF>(a.gpre, i);
                 }
@@ -102,7 +109,7 @@ __global__ __launch_bounds__(256) void beam_combine_norm(CombineArgs a) {
 #pragma unroll
             for (int it = 0; it < NIT; ++it) {
                 const int i = (it * 256 + tid) * 4;
-                yv[j][it] = (rr[j] >= 0 && i < H) ? ld4<YBF>(a.y, (size_t)rr[j] * H + i)
+                yv[j][it] = (rr[j] >= 0 && i < H) ? ld4<YBF, true>(a.y, (size_t)rr[j] * H + i)
                                                   : make_float4(0.f, 0.f, 0.f, 0.f);
             }
 #pragma unroll
@@ -137,7 +144,7 @@ __global__ __launch_bounds__(256) void beam_combine_norm(CombineArgs a) {
         if (i < H) {
             if (a.moe_out) *reinterpret_cast<float4*>(a.moe_out + rowo + i) = m[it];
             const float4 g = kEager ? gpo[kEager ? it : 0] : ld4<ABF>(a.gpost, i);
-            const float4 h = kEager ? hv[kEager ? it : 0] : ld4<ABF>(a.h, rowo + i);
+            const float4 h = kEager ? hv[kEager ? it : 0] : ld4<ABF, true>(a.h, rowo + i);
             float4 hn;
             hn.x = rnd_act<ABF>(a.c_res * h.x + a.c_new * rnd_act<ABF>(m[it].x * rinv * g.x));
             hn.y = rnd_act<ABF>(a.c_res * h.y + a.c_new * rnd_act<ABF>(m[it].y * rinv * g.y));
