@@ -441,8 +441,12 @@ beam_status beam_moe_dense_mlp(const beam_moe_cfg* cfg, int32_t T, int32_t d_ff,
     if (S > 1) after += align256((size_t)S * T * H * sizeof(float));
     float* g1_parts = S1 > 1 ? reinterpret_cast<float*>(after) : nullptr;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (beam::launch_dense_rows(T, offsets, row_token, st) != hipSuccess) return BEAM_ERR_HIP;
+    // the identity routing (one expert holding tokens 0..T-1 in order); the
+    // direct kernels of small batches take it without reading it
+    const bool identity = beam::experts_direct_path(T);
+    if (!identity && beam::launch_dense_rows(T, offsets, row_token, st) != hipSuccess) return BEAM_ERR_HIP;
     beam::ExpertsArgs a{};
+    a.identity_rows = identity;
     a.T = T;
     a.K = 1;
     a.E = 1;

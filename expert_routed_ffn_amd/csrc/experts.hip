@@ -141,6 +141,7 @@ struct GemmParams {
     const int32_t* offsets;
     int E;
     int* unit_ctr;             // wide path: 8 unit counters, one per XCD, zero at launch
+    int identity_rows;         // direct path: > 0 = one expert whose rows are tokens 0..identity_rows-1
 };
 
 template <int V> struct IC { static constexpr int value = V; };
@@ -270,7 +271,7 @@ BEAM_DEV void gemm_item_direct(const GemmParams& p, int e, int row0, int rows, i
     int tok;
     const uint8_t* pb;
     if constexpr (G1) {
-        tok = bval ? p.row_token[row0 + r] : 0;
+        tok = bval ? (p.identity_rows ? row0 + r : p.row_token[row0 + r]) : 0;
         pb = p.act + (size_t)tok * krow + 16 * g;
     } else {
         tok = row0 + r;
@@ -559,8 +560,12 @@ template <int KIND, bool G1>
 __global__ __launch_bounds__(256) void beam_expert_gemm_direct(GemmParams p) {
     const int item = blockIdx.x / p.n_tiles;
     const int tile = blockIdx.x - item * p.n_tiles;
-    int e, row0, rows;
-    if (!direct_item(p.offsets, p.E, item, e, row0, rows)) return;
+    int e = 0, row0 = 0, rows = p.identity_rows;
+    if (p.identity_rows) {
+        if (item > 0) return;
+    } else if (!direct_item(p.offsets, p.E, item, e, row0, rows)) {
+        return;
+    }
     gemm_item_direct<KIND, G1>(p, e, row0, rows, tile);
 }
 
@@ -1114,8 +1119,10 @@ static size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 //              (beam_expert_gemm_wide).
 enum GemmPath { PATH_DIRECT, PATH_LDS, PATH_WIDE };
 
+bool experts_direct_path(int T) { return T <= 16; }
+
 static GemmPath gemm_path(int T, int K, int E) {
-    if (T <= 16) return PATH_DIRECT;
+    if (experts_direct_path(T)) return PATH_DIRECT;
     return (long long)T * K >= 256LL * E ? PATH_WIDE : PATH_LDS;
 }
 
@@ -1238,6 +1245,7 @@ hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st) {
     p.offsets = a.offsets;
     p.E = a.E;
     p.unit_ctr = ws.unit_ctr;
+    p.identity_rows = (a.identity_rows && path == PATH_DIRECT) ? a.T : 0;
     p.H = a.H;
     p.F = a.F;
     p.ksplit = 1;

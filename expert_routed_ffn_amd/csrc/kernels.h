@@ -69,7 +69,12 @@ struct ExpertsArgs {
     // (fp32), and a fixed-order sum over the slices applies SwiGLU
     int ksplit1 = 1;
     float* g1_parts = nullptr;
+    // one expert whose rows are the T tokens in order (a dense MLP): on the
+    // direct path (T <= 16) offsets and row_token are then not read
+    bool identity_rows = false;
 };
+// whether launch_experts takes the direct path (T <= 16 tokens)
+bool experts_direct_path(int T);
 size_t experts_ws_bytes(int T, int K, int E, int H, int F, WKind w);
 hipError_t launch_experts(const ExpertsArgs& a, hipStream_t st);
 
