@@ -1,18 +1,21 @@
 // Grouped SwiGLU experts: GEMM1 (gate and up projections with SwiGLU fused
 // into the epilogue) and GEMM2 (down projection) over the expert-grouped
-// rows, bf16 or fp8-e4m3 on MFMA, plus a plain fp32 path for small shapes.
+// rows, bf16, fp8-e4m3 or MXFP4 on MFMA, plus a plain fp32 path for small
+// shapes.
 // (TokenSpeed x Reflection Beam blog, "TensorRT-LLM NVFP4 MoE": both expert
-//  GEMMs with SwiGLU fused into the first; Gaudi cookbook, "What was built"
-//  and "EP vs TP quality": per-channel FP8 weights, dynamic per-token
-//  activations, down-projection input quantised per token over all d_ff.)
+//  GEMMs with SwiGLU fused into the first; "NVFP4 and FP8 checkpoints":
+//  4-bit weights; Gaudi cookbook, "What was built" and "EP vs TP quality":
+//  per-channel FP8 weights, dynamic per-token activations, down-projection
+//  input quantised per token over all d_ff.)
 //
 // Work decomposition.  A work item is (expert e, up to MC consecutive
-// permuted rows of e); items are built on the device from the expert
-// offsets, so the host never reads routing results.  A 256-thread
-// workgroup takes one item and one N-tile of weight rows; each of its 4
-// waves owns two 16-row MFMA tiles of weights (GEMM1: 16 gate rows and the
-// 16 matching up rows, so SwiGLU happens in registers; GEMM2: 32 output
-// rows) and the item's rows in blocks of 16.  Weights stream from HBM
+// permuted rows of e), taken from the expert offsets on the device, so the
+// host never reads routing results (the direct kernels find their item in
+// the offsets; the others read a list a one-block kernel builds).  A
+// 256-thread workgroup takes one item and one N-tile of weight rows; each
+// of its 4 waves owns two 16-row MFMA tiles of weights (four on the wide
+// path) -- GEMM1: gate rows and the matching up rows, so SwiGLU happens in
+// registers; GEMM2: output rows -- and the item's rows in blocks of 16.  Weights stream from HBM
 // straight into MFMA A-operand registers, each weight byte read once per
 // item, from the packed layout (pack.hip): every weight load instruction of
 // a wave reads 1 KiB of contiguous whole cache lines, non-temporally.
@@ -21,6 +24,8 @@
 // packed A fragment holds.  bf16: MFMA step s uses piece s.  fp8: MFMA step
 // t uses pieces 2t and 2t+1 (32 bytes = the lane's 32 k values).
 #include <type_traits>
+
+#include <atomic>
 
 #include "common.h"
 #include "kernels.h"
@@ -1187,17 +1192,18 @@ size_t experts_ws_bytes(int T, int K, int E, int H, int F, WKind w) {
 }
 
 
-// compute units of the current device (looked up once per device)
+// compute units of the current device (looked up once per device; calls
+// from several host threads may look it up concurrently, harmlessly)
 static int device_cus() {
-    static int cus[64];
+    static std::atomic<int> cus[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cus[dev] <= 0) {
-        int n = 0;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cus[dev] = n;
+        cus[dev].store(n, std::memory_order_relaxed);
     }
-    return cus[dev];
+    return n;
 }
 
 template <int KIND, bool G1>
