@@ -47,6 +47,32 @@ BEAM_DEV uint32_t f32_to_e4m3(float f) {
     return sign | (r - (120u << 3));                   // rebias exponent 127 -> 7
 }
 
+// Four values to OCP E4M3FN codes (byte j = value j), bit for bit as
+// f32_to_e4m3: gfx950's conversion instruction rounds to nearest even and
+// agrees with that formula for every fp32 input below 464 in magnitude (a
+// check over all 2^32 inputs on MI355X); larger values are clamped to
+// +-448 first (the saturated code 0x7E), and a NaN keeps its sign bit
+// (0x7F / 0xFF), which the instruction does not.
+BEAM_DEV uint32_t e4m3x4(float a, float b, float c, float d) {
+    const float v[4] = {a, b, c, d};
+    float w[4];
+    bool any_nan = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        w[j] = fminf(fmaxf(v[j], -448.0f), 448.0f);
+        any_nan |= v[j] != v[j];
+    }
+    uint32_t r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(w[0], w[1], 0, false);
+    r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(w[2], w[3], (int)r, true);
+    if (any_nan) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (v[j] != v[j])
+                r = (r & ~(0xFFu << (8 * j))) | ((((__float_as_uint(v[j]) >> 24) & 0x80u) | 0x7Fu) << (8 * j));
+    }
+    return r;
+}
+
 // ---------------------------------------------------------------- reductions
 
 BEAM_DEV float wave_sum(float v) {
@@ -128,10 +154,8 @@ BEAM_DEV void quantize_row_e4m3(Load4 load4, int n, uint8_t* __restrict__ q, flo
     for (int it = 0; it < kQuantMaxIter; ++it) {
         const int i = (it * 256 + threadIdx.x) * 4;
         if (i < n) {
-            uint32_t c = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) c |= f32_to_e4m3(__fdiv_rn(v[it][j], s)) << (8 * j);
-            *reinterpret_cast<uint32_t*>(q + i) = c;
+            *reinterpret_cast<uint32_t*>(q + i) = e4m3x4(__fdiv_rn(v[it][0], s), __fdiv_rn(v[it][1], s),
+                                                         __fdiv_rn(v[it][2], s), __fdiv_rn(v[it][3], s));
         }
     }
     if (threadIdx.x == 0) *scale_out = s;
@@ -162,10 +186,8 @@ BEAM_DEV void quantize_row_e4m3_wave(Load4 load4, int n, uint8_t* __restrict__ q
     for (int it = 0; it < NIT; ++it) {
         const int i = (it * 64 + lane) * 4;
         if (i < n) {
-            uint32_t c = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) c |= f32_to_e4m3(__fdiv_rn(v[it][j], s)) << (8 * j);
-            *reinterpret_cast<uint32_t*>(q + i) = c;
+            *reinterpret_cast<uint32_t*>(q + i) = e4m3x4(__fdiv_rn(v[it][0], s), __fdiv_rn(v[it][1], s),
+                                                         __fdiv_rn(v[it][2], s), __fdiv_rn(v[it][3], s));
         }
     }
     if (lane == 0) *scale_out = s;
