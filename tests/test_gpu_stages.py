@@ -278,6 +278,68 @@ def test_quantize_mx_bit_exact():
         np.testing.assert_array_equal(oracle.unpack_fp4(xq.cpu().numpy()), oracle.e2m1_encode(q_o))
 
 
+def test_quantizers_special_values():
+    # the documented handling of NaN and infinite inputs by the run-time
+    # quantisers (include/beam_moe.h): e4m3 -- NaN stays out of the row
+    # maximum and gets a NaN code, an infinite element makes the scale
+    # infinite, the row's finite elements code 0 and the infinite ones NaN;
+    # MXFP4 -- NaN and +-Inf are stored as +-6
+    say("quantisers on NaN and infinite inputs")
+    T, H = 4, 5120
+    g = torch.Generator(device=DEV).manual_seed(9)
+    x = torch.randn((T, H), generator=g, device=DEV).to(torch.bfloat16)
+    x[0, 17] = float("nan")
+    x[0, 4000] = -float("nan")
+    x[1, 5] = float("inf")
+    x[2, 3000] = -float("inf")
+    cfg = beam.LayerCfg()
+    xq = torch.empty((T, H), dtype=torch.uint8, device=DEV)
+    xs = torch.empty(T, dtype=torch.float32, device=DEV)
+    beam.beam_moe_quantize_fp8(cfg, x, xq, xs)
+    mq = torch.empty((T, H // 2), dtype=torch.uint8, device=DEV)
+    ms = torch.empty((T, H // 32), dtype=torch.uint8, device=DEV)
+    beam.beam_moe_quantize_mx(cfg, x, mq, ms)
+    torch.cuda.synchronize()
+    xn = synth.to_f64(x)
+    codes = xq.cpu().numpy()
+    q_gpu = oracle.e4m3_decode(codes)
+    s_gpu = xs.cpu().double().numpy()
+    # row 0: scale and codes of the row without its NaN elements
+    nan_at = [17, 4000]
+    clean = np.delete(xn[0], nan_at)
+    s0, q0 = oracle.quantize_row_e4m3(clean)
+    assert s_gpu[0] == s0
+    assert np.array_equal(np.delete(q_gpu[0], nan_at), q0)
+    assert all(np.isnan(q_gpu[0, i]) for i in nan_at)
+    # rows 1 and 2: infinite scale, finite elements 0, the infinite one NaN
+    for t, i in ((1, 5), (2, 3000)):
+        assert np.isinf(s_gpu[t])
+        assert np.isnan(q_gpu[t, i])
+        assert np.all(np.delete(q_gpu[t], i) == 0.0)
+    # row 3 is ordinary
+    s3, q3 = oracle.quantize_row_e4m3(xn[3])
+    assert s_gpu[3] == s3 and np.array_equal(q_gpu[3], q3)
+    # MXFP4: the special elements hold the code of +-6, the other blocks of
+    # the rows are the oracle's
+    c = oracle.unpack_fp4(mq.cpu().numpy())
+    vals = oracle.e2m1_decode(c)
+    bits = x.view(torch.int16).cpu().numpy()   # the sign bit as stored (a NaN's too)
+    for t, i in ((0, 17), (0, 4000), (1, 5), (2, 3000)):
+        sign = -1.0 if bits[t, i] < 0 else 1.0
+        assert vals[t, i] == 6.0 * sign, (t, i, vals[t, i])
+    s_o, q_o = oracle.quantize_mx_fp4(xn[3:4])
+    assert np.array_equal(ms.cpu().numpy()[3:4], s_o)
+    assert np.array_equal(c[3:4], oracle.e2m1_encode(q_o))
+    special_blocks = {(0, 17 // 32), (0, 4000 // 32), (1, 5 // 32), (2, 3000 // 32)}
+    for t in range(3):
+        for b in range(H // 32):
+            if (t, b) in special_blocks:
+                continue
+            s_b, q_b = oracle.quantize_mx_fp4(xn[t:t + 1, 32 * b:32 * b + 32])
+            assert ms.cpu().numpy()[t, b] == s_b[0, 0], (t, b)
+            assert np.array_equal(c[t, 32 * b:32 * b + 32], oracle.e2m1_encode(q_b)[0]), (t, b)
+
+
 def test_experts_every_token_on_one_expert():
     say("experts: 150 rows on one expert (items of 128 + 22 rows)")
     wl = _stage_wl("bf16", H=512, F=256)
