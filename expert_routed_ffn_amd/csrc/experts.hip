@@ -707,11 +707,18 @@ BEAM_DEV void gemm_item_wide(const GemmParams& p, int e, int row0, int rows, int
     const int kblk = (G1 ? p.H : p.F) / 32;
     const uint8_t* psw[4] = {nullptr, nullptr, nullptr, nullptr};
     if constexpr (MX) {
-        for (int q = threadIdx.x; q < kWideRows * nk; q += 256) {
-            const int rr = q / nk, c = q - rr * nk;
-            const int src = rr < rows ? rr : 0;
-            const size_t srow_mx = G1 ? (size_t)p.row_token[row0 + src] : (size_t)(row0 + src);
-            ssc[rr * 16 + c] = ld16(p.mx_act + srow_mx * kblk + c * 16);
+        // two threads per item row, each copying every other 16-code chunk
+        // of the row's whole K (nk <= 16: K <= 8192): one row-map load, then
+        // up to eight independent loads (a loop over all 128 x nk chunks
+        // made each thread wait on five row-map / code load pairs in turn)
+        const int rr = threadIdx.x >> 1, c0 = threadIdx.x & 1;
+        const int src = rr < rows ? rr : 0;
+        const size_t srow_mx = G1 ? (size_t)p.row_token[row0 + src] : (size_t)(row0 + src);
+        const uint8_t* pmx = p.mx_act + srow_mx * kblk;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int c = c0 + 2 * i;
+            if (c < nk) ssc[rr * 16 + c] = ld16(pmx + c * 16);
         }
         const size_t wrow0 = (size_t)e * (G1 ? 2 * p.F : p.H);
 #pragma unroll
