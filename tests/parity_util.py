@@ -23,7 +23,7 @@ NEAR_TIE = 1e-6
 W_RTOL = 1e-5
 BF16_MAXABS, BF16_RELL2 = 2e-2, 5e-3
 FP8_RELL2 = 3e-2
-# 4-bit (MXFP4) experts: the benchmark spec states no bound for them; the
+# 4-bit (MXFP4) experts: the stated targets give no bound for them; the
 # quantised-path bound of the fp8 experts (rel-L2 3e-2 against the oracle
 # of the same quantised arithmetic) is taken for them too
 MX_RELL2 = 3e-2
