@@ -30,7 +30,8 @@
  *     shared by the calls of one layer on one stream; calls that overlap in
  *     time must not share one.
  *   - Calls on one stream are ordered; the library keeps no state between
- *     calls, so calls on different streams or threads are independent.
+ *     calls (other than each device's compute-unit count, looked up once),
+ *     so calls on different streams or threads are independent.
  */
 #ifndef BEAM_MOE_H
 #define BEAM_MOE_H
