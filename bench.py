@@ -16,9 +16,11 @@ one JSON line.
     (--workload dense_t8 / dense_t2048 / ep8_shard_t8 / ep8_shard_t2048 prints
     that row's entry alone, for profiling runs)
 
-Timing: HIP events recorded on the launch stream around every C-ABI call
-of every timed step (route, permute, experts, combine_norm), plus one pair
-around the whole timed region; `ms_per_step` is the region over K.  The
+Timing: one pair of HIP events on the launch stream around the whole timed
+region (`ms_per_step` is the region over K) and one pair around the experts
+call of every timed step; the per-stage times (route, permute, experts,
+combine_norm) come from a second pass of K steps with an event after every
+C-ABI call, so that those markers do not sit inside the timed region.  The
 `roofline` object describes the dominant call, beam_moe_experts (its
 work-item, GEMM1 + SwiGLU and GEMM2 kernels), against HBM or MFMA peak
 depending on the rows per touched expert.  A hipGraph replay of the same
@@ -188,17 +190,20 @@ def layer_setup(wl, stacks, dev):
                 wgu=wgu, wd=wd, sgu=sgu, sd=sd, fp8=fp8, mx=mx, side=side)
 
 
-def run_step(wl, s, hipev=None, evs=None, stream=None):
+def run_step(wl, s, hipev=None, evs=None, stream=None, marks=(0, 1, 2, 3, 4)):
     """One layer step through the C-ABI calls; with evs (5 events) an event
     is recorded on the launch stream before the first call and after the
-    route, permute, experts and combine_norm calls.  With 8-bit or 4-bit
+    route, permute, experts and combine_norm calls (only those of them that
+    `marks` lists, so the timed steps carry no more markers than the
+    roofline needs).  With 8-bit or 4-bit
     experts the input quantisation runs either on a second stream alongside
     the route and permute calls (the experts call waits for it) or in line,
     in the route stage (MXFP4) or inside the permute call (e4m3)."""
     import torch
     import expert_routed_ffn_amd as beam
     cfg, b = s["cfg"], s["bufs"]
-    mark = (lambda i: hipev.record(evs[i], stream)) if evs is not None else (lambda i: None)
+    mark = (lambda i: hipev.record(evs[i], stream) if i in marks else None) if evs is not None \
+        else (lambda i: None)
     side = s["side"]
     mark(0)
     if side is not None:
@@ -234,29 +239,35 @@ def stats(v):
 
 
 def time_workload(wl, stacks, steps, warmup, hipev, dev, graph=True):
-    """Per-step stage times (µs), the timed region per step, touched experts
-    and (optionally) the hipGraph replay time per step."""
+    """The timed region per step, the experts call's time in each timed step
+    (events around that call only), touched experts, per-step stage times
+    (µs) from a second, fully marked pass of the same number of steps after
+    the timed region, and (optionally) the hipGraph replay time per step."""
     import torch
     s = layer_setup(wl, stacks, dev)
     stream = torch.cuda.current_stream().cuda_stream
     evs = [[hipev.create() for _ in range(5)] for _ in range(steps)]
+    evs2 = [[hipev.create() for _ in range(5)] for _ in range(steps)]
     t0, t1 = hipev.create(), hipev.create()
     for _ in range(warmup):
         run_step(wl, s)
     torch.cuda.synchronize()
     hipev.record(t0, stream)
     for i in range(steps):
-        run_step(wl, s, hipev, evs[i], stream)
+        run_step(wl, s, hipev, evs[i], stream, marks=(2, 3))
     hipev.record(t1, stream)
     torch.cuda.synchronize()
     region_ms = hipev.elapsed_ms(t0, t1)
+    for i in range(steps):
+        run_step(wl, s, hipev, evs2[i], stream)
+    torch.cuda.synchronize()
     per = {k: [] for k in ("layer", "route", "permute", "experts", "combine_norm")}
-    for e in evs:
-        per["layer"].append(hipev.elapsed_ms(e[0], e[4]) * 1e3)
-        per["route"].append(hipev.elapsed_ms(e[0], e[1]) * 1e3)
-        per["permute"].append(hipev.elapsed_ms(e[1], e[2]) * 1e3)
+    for e, f in zip(evs, evs2):
         per["experts"].append(hipev.elapsed_ms(e[2], e[3]) * 1e3)
-        per["combine_norm"].append(hipev.elapsed_ms(e[3], e[4]) * 1e3)
+        per["layer"].append(hipev.elapsed_ms(f[0], f[4]) * 1e3)
+        per["route"].append(hipev.elapsed_ms(f[0], f[1]) * 1e3)
+        per["permute"].append(hipev.elapsed_ms(f[1], f[2]) * 1e3)
+        per["combine_norm"].append(hipev.elapsed_ms(f[3], f[4]) * 1e3)
     offs = s["bufs"].expert_offsets.cpu()
     D = int(((offs[1:] - offs[:-1]) > 0).sum())
     out = dict(ms_per_step=region_ms / steps, per=per, touched=D, state=s)

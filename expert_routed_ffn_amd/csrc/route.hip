@@ -283,18 +283,39 @@ __global__ __launch_bounds__(256) void beam_route_select(
     if (t >= T) return;   // whole wave exits together
     const size_t TE = (size_t)T * E;
 
+    // logits = partial sums over the K slices, added in slice order; the
+    // loads of four slices of all EPL experts are issued together, so the
+    // partials cost one memory round trip per four slices, not one per
+    // (slice, expert)
+    constexpr int kSl = 4;
+    const size_t at0 = (size_t)t * E + lane * EPL;
+    float z[EPL], bi[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        z[i] = 0.f;
+        bi[i] = lane * EPL + i < E ? bias[lane * EPL + i] : 0.f;
+    }
+    for (int sl0 = 0; sl0 < nsplit; sl0 += kSl) {
+        float q[kSl][EPL];
+#pragma unroll
+        for (int j = 0; j < kSl; ++j)
+#pragma unroll
+            for (int i = 0; i < EPL; ++i)
+                q[j][i] = (sl0 + j < nsplit && lane * EPL + i < E) ? part[(size_t)(sl0 + j) * TE + at0 + i] : 0.f;
+#pragma unroll
+        for (int j = 0; j < kSl; ++j)
+#pragma unroll
+            for (int i = 0; i < EPL; ++i)
+                if (sl0 + j < nsplit) z[i] = sl0 + j == 0 ? q[j][i] : z[i] + q[j][i];
+    }
     float s[EPL], b[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = lane * EPL + i;
         if (e < E) {
-            // logits = partial sums over the K slices, added in slice order
-            const size_t at = (size_t)t * E + e;
-            float z = part[at];
-            for (int sl = 1; sl < nsplit; ++sl) z += part[sl * TE + at];
-            if (logits_out && logits_out != part) logits_out[at] = z;
-            s[i] = 1.0f / (1.0f + expf(-z));
-            b[i] = s[i] + bias[e];
+            if (logits_out && logits_out != part) logits_out[at0 + i] = z[i];
+            s[i] = 1.0f / (1.0f + expf(-z[i]));
+            b[i] = s[i] + bi[i];
         } else {
             s[i] = 0.f;
             b[i] = -INFINITY;
