@@ -17,22 +17,41 @@ namespace beam {
 constexpr int kMaxIt = 8;    // chunks of 4 per thread: H <= 8 * 1024
 constexpr int kSmallT = 256; // up to this many tokens the grid is too small to hide latency
 
-// 4 consecutive elements as fp32; NT: a streaming (non-temporal) load, for
-// data this kernel reads once (the expert rows y, the token's h), which
-// should not push the reused gammas out of the caches
-template <bool BF, bool NT = false> BEAM_DEV float4 ld4(const void* p, size_t i) {
+// 4 consecutive elements as loaded (two bf16 pairs or four fp32), then
+// widened to fp32 in a separate step: a widening next to its load would make
+// the load's wait come right after it, so keeping the raw bits lets a
+// thread have all its loads in flight before the first one is used.  NT: a
+// streaming (non-temporal) load, for data this kernel reads once (the
+// expert rows y, the token's h), which should not push the reused gammas
+// out of the caches.
+template <bool BF> struct Raw4;
+template <> struct Raw4<true> { uint2 v; };
+template <> struct Raw4<false> { float4 v; };
+template <bool BF, bool NT = false> BEAM_DEV Raw4<BF> ldr4(const void* p, size_t i) {
+    Raw4<BF> r;
     if constexpr (BF) {
         typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
         const u32x2v* q = reinterpret_cast<const u32x2v*>(static_cast<const uint16_t*>(p) + i);
         const u32x2v u = NT ? __builtin_nontemporal_load(q) : *q;
-        return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
-                           __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+        r.v = make_uint2(u.x, u.y);
     } else {
         typedef float f32x4v __attribute__((ext_vector_type(4)));
         const f32x4v* q = reinterpret_cast<const f32x4v*>(static_cast<const float*>(p) + i);
         const f32x4v v = NT ? __builtin_nontemporal_load(q) : *q;
-        return make_float4(v.x, v.y, v.z, v.w);
+        r.v = make_float4(v.x, v.y, v.z, v.w);
     }
+    return r;
+}
+template <bool BF> BEAM_DEV Raw4<BF> zero4() {
+    Raw4<BF> r;
+    if constexpr (BF) r.v = make_uint2(0u, 0u);
+    else r.v = make_float4(0.f, 0.f, 0.f, 0.f);
+    return r;
+}
+BEAM_DEV float4 wid4(Raw4<false> r) { return r.v; }
+BEAM_DEV float4 wid4(Raw4<true> r) {
+    return make_float4(__uint_as_float(r.v.x << 16), __uint_as_float(r.v.x & 0xFFFF0000u),
+                       __uint_as_float(r.v.y << 16), __uint_as_float(r.v.y & 0xFFFF0000u));
 }
 template <bool BF> BEAM_DEV float rnd_act(float v) {
     if constexpr (BF) return bf16_to_f32(f32_to_bf16(v));
@@ -59,6 +78,8 @@ BEAM_DEV float4 fma4(float w, float4 y, float4 m) {
 // trips to memory instead of five; with many tokens one row at a time
 // leaves registers for the most resident waves (measured on MI355X at
 // 16384 tokens with bf16 y: 569 us with 4 rows at a time, 405 us with one).
+// Every group of loads (a row's chunks, the residual's h and gamma chunks,
+// the pre-norm gamma chunks) is issued whole before any of it is used.
 template <bool YBF, bool ABF, int NIT, int RG>
 __global__ __launch_bounds__(256) void beam_combine_norm(CombineArgs a) {
     __shared__ float red[4];
@@ -73,18 +94,26 @@ __global__ __launch_bounds__(256) void beam_combine_norm(CombineArgs a) {
 
     const size_t rowo = (size_t)t * H;
     constexpr bool kEager = RG >= 8;
-    float4 hv[kEager ? NIT : 1], gpo[kEager ? NIT : 1], gpr[kEager ? NIT : 1];
+    Raw4<ABF> hv[NIT], gpo[NIT], gpr[NIT];
+    auto load_res = [&](Raw4<ABF>* hh, Raw4<ABF>* gg) {   // residual operands: h and the post-norm gamma
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int i = (it * 256 + tid) * 4;
+            hh[it] = i < H ? ldr4<ABF, true>(a.h, rowo + i) : zero4<ABF>();
+            gg[it] = i < H ? ldr4<ABF>(a.gpost, i) : zero4<ABF>();
+        }
+    };
+    auto load_pre = [&](Raw4<ABF>* gg) {                  // the pre-norm gamma
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int i = (it * 256 + tid) * 4;
+            gg[it] = i < H ? ldr4<ABF>(a.gpre, i) : zero4<ABF>();
+        }
+    };
     if constexpr (kEager) {
         if (!a.partial_only) {
-#pragma unroll
-            for (int it = 0; it < NIT; ++it) {
-                const int i = (it * 256 + tid) * 4;
-                if (i < H) {
-                    hv[it] = ld4<ABF, true>(a.h, rowo + i);
-                    gpo[it] = ld4<ABF>(a.gpost, i);
-                    gpr[it] = ld4<ABF>(a.gpre, i);
-                }
-            }
+            load_res(hv, gpo);
+            load_pre(gpr);
         }
     }
     float4 m[NIT];
@@ -103,19 +132,18 @@ __global__ __launch_bounds__(256) void beam_combine_norm(CombineArgs a) {
             rr[j] = ((unsigned)r < (unsigned)TK) ? r : -1;   // never read outside y
             wk[j] = k < K ? (wrow ? wrow[k] : 1.0f) : 0.f;
         }
-        float4 yv[RG][NIT];
+        Raw4<YBF> yv[RG][NIT];
 #pragma unroll
         for (int j = 0; j < RG; ++j)
 #pragma unroll
             for (int it = 0; it < NIT; ++it) {
                 const int i = (it * 256 + tid) * 4;
-                yv[j][it] = (rr[j] >= 0 && i < H) ? ld4<YBF, true>(a.y, (size_t)rr[j] * H + i)
-                                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+                yv[j][it] = (rr[j] >= 0 && i < H) ? ldr4<YBF, true>(a.y, (size_t)rr[j] * H + i) : zero4<YBF>();
             }
 #pragma unroll
         for (int j = 0; j < RG; ++j)
 #pragma unroll
-            for (int it = 0; it < NIT; ++it) m[it] = fma4(wk[j], yv[j][it], m[it]);
+            for (int it = 0; it < NIT; ++it) m[it] = fma4(wk[j], wid4(yv[j][it]), m[it]);
     }
 
     if (a.partial_only) {   // one expert-parallel shard's share of m: no norm
@@ -126,6 +154,7 @@ __global__ __launch_bounds__(256) void beam_combine_norm(CombineArgs a) {
         }
         return;
     }
+    if constexpr (!kEager) load_res(hv, gpo);   // in flight during the post-norm reduction
 
     // post-norm
     float ss = 0.f;
@@ -143,8 +172,8 @@ __global__ __launch_bounds__(256) void beam_combine_norm(CombineArgs a) {
         const int i = (it * 256 + tid) * 4;
         if (i < H) {
             if (a.moe_out) *reinterpret_cast<float4*>(a.moe_out + rowo + i) = m[it];
-            const float4 g = kEager ? gpo[kEager ? it : 0] : ld4<ABF>(a.gpost, i);
-            const float4 h = kEager ? hv[kEager ? it : 0] : ld4<ABF, true>(a.h, rowo + i);
+            const float4 g = wid4(gpo[it]);
+            const float4 h = wid4(hv[it]);
             float4 hn;
             hn.x = rnd_act<ABF>(a.c_res * h.x + a.c_new * rnd_act<ABF>(m[it].x * rinv * g.x));
             hn.y = rnd_act<ABF>(a.c_res * h.y + a.c_new * rnd_act<ABF>(m[it].y * rinv * g.y));
@@ -154,6 +183,7 @@ __global__ __launch_bounds__(256) void beam_combine_norm(CombineArgs a) {
             ss2 += (hn.x * hn.x + hn.y * hn.y) + (hn.z * hn.z + hn.w * hn.w);
         }
     }
+    if constexpr (!kEager) load_pre(gpr);   // in flight during the pre-norm reduction
     ss2 = block_sum<4>(ss2, red);
     const float rinv2 = 1.0f / sqrtf(ss2 / (float)H + a.eps);
 #pragma unroll
@@ -161,7 +191,7 @@ __global__ __launch_bounds__(256) void beam_combine_norm(CombineArgs a) {
         const int i = (it * 256 + tid) * 4;
         if (i < H) {
             st4<ABF>(a.h, rowo + i, m[it]);
-            const float4 g = kEager ? gpr[kEager ? it : 0] : ld4<ABF>(a.gpre, i);
+            const float4 g = wid4(gpr[it]);
             st4<ABF>(a.x_next, rowo + i,
                      make_float4(m[it].x * rinv2 * g.x, m[it].y * rinv2 * g.y, m[it].z * rinv2 * g.z,
                                  m[it].w * rinv2 * g.w));

@@ -27,42 +27,79 @@ template <> BEAM_DEV float4 ld_x4<uint16_t>(const uint16_t* p) {
 // tokens with it (the pages' <=16-token GEMV design, re-tiled for
 // 256-thread workgroups and split over K so that each thread has little
 // serial work); the selection kernel adds the slices in slice order.
+// Each thread covers NIT chunks of 4 values of the slice.  The loads of a
+// batch of tokens are all issued before the first multiply-add, so the
+// activations cost one memory round trip per batch rather than one per
+// (token, chunk).
 // ---------------------------------------------------------------------------
 constexpr int kSmallT = 16;
 
-template <typename XT>
+template <typename XT> struct XRaw;                      // 4 activations as loaded
+template <> struct XRaw<uint16_t> { uint2 v; };
+template <> struct XRaw<float> { float4 v; };
+template <typename XT> BEAM_DEV XRaw<XT> ld_xraw(const XT* p) {
+    XRaw<XT> r;
+    if constexpr (sizeof(XT) == 2) r.v = *reinterpret_cast<const uint2*>(p);
+    else r.v = *reinterpret_cast<const float4*>(p);
+    return r;
+}
+BEAM_DEV float4 widen(XRaw<float> r) { return r.v; }
+BEAM_DEV float4 widen(XRaw<uint16_t> r) {
+    return make_float4(__uint_as_float(r.v.x << 16), __uint_as_float(r.v.x & 0xFFFF0000u),
+                       __uint_as_float(r.v.y << 16), __uint_as_float(r.v.y & 0xFFFF0000u));
+}
+
+template <typename XT, int NIT, int TB>
 __global__ __launch_bounds__(256) void beam_router_logits_small(
     const XT* __restrict__ x, const float* __restrict__ w, float* __restrict__ logits,
     int T, int H, int E, int kslice) {
-    constexpr int kMaxIt = 8;   // kslice <= 8 * 1024
+    // tokens whose loads are in flight together: TB (8 when T <= 8, else
+    // 16), at most about 64 registers of raw activations per thread.  Past
+    // T a batch re-reads token T-1 (a load under a token condition would
+    // be waited for before the next one is issued).
+    constexpr int kCap = 64 / (NIT * (int)sizeof(XT));
+    constexpr int kBatch = TB < kCap ? TB : kCap;
     __shared__ float red[4][kSmallT];
     const int e = blockIdx.x;
     const int k0 = blockIdx.y * kslice, k1 = k0 + kslice;
     const float* wr = w + (size_t)e * H;
     logits += (size_t)blockIdx.y * T * E;
-    // all of this thread's router weights first (one latency for the row)
-    float4 wv[kMaxIt];
+    float4 wv[NIT];
+    bool ok[NIT];
+    int kk[NIT];
 #pragma unroll
-    for (int it = 0; it < kMaxIt; ++it) {
+    for (int it = 0; it < NIT; ++it) {
         const int k = k0 + (it * 256 + threadIdx.x) * 4;
-        wv[it] = k < k1 ? *reinterpret_cast<const float4*>(wr + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+        ok[it] = k < k1;
+        kk[it] = ok[it] ? k : k0;   // chunks past the slice read its first chunk and are not used
+        wv[it] = *reinterpret_cast<const float4*>(wr + kk[it]);
     }
+    __builtin_amdgcn_sched_barrier(0);   // the weight loads go out first
     float acc[kSmallT];
 #pragma unroll
-    for (int t = 0; t < kSmallT; ++t) {
-        acc[t] = 0.f;
-        if (t < T) {
+    for (int t0 = 0; t0 < kSmallT; t0 += kBatch) {
+        if (t0 >= T) break;
+        XRaw<XT> xr[kBatch][NIT];
 #pragma unroll
-            for (int it = 0; it < kMaxIt; ++it) {
-                const int k = k0 + (it * 256 + threadIdx.x) * 4;
-                if (k < k1) {
-                    const float4 xv = ld_x4<XT>(x + (size_t)t * H + k);
-                    acc[t] = fmaf(xv.x, wv[it].x, acc[t]);
-                    acc[t] = fmaf(xv.y, wv[it].y, acc[t]);
-                    acc[t] = fmaf(xv.z, wv[it].z, acc[t]);
-                    acc[t] = fmaf(xv.w, wv[it].w, acc[t]);
+        for (int j = 0; j < kBatch; ++j) {
+            const int t = t0 + j < T ? t0 + j : T - 1;
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) xr[j][it] = ld_xraw<XT>(x + (size_t)t * H + kk[it]);
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            float a = 0.f;
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) {
+                if (ok[it]) {
+                    const float4 xv = widen(xr[j][it]);
+                    a = fmaf(xv.x, wv[it].x, a);
+                    a = fmaf(xv.y, wv[it].y, a);
+                    a = fmaf(xv.z, wv[it].z, a);
+                    a = fmaf(xv.w, wv[it].w, a);
                 }
             }
+            acc[t0 + j] = a;
         }
     }
     const int lane = threadIdx.x & 63, wq = threadIdx.x >> 6;
@@ -451,12 +488,24 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
     float* part = (nsplit == 1 && a.logits_out) ? a.logits_out : a.partials;
     if (T <= kSmallT) {
         const dim3 grid(E, nsplit);
-        if (a.x_bf16)
-            hipLaunchKernelGGL(beam_router_logits_small<uint16_t>, grid, dim3(256), 0, st,
-                               (const uint16_t*)a.x, a.w, part, T, H, E, H / nsplit);
-        else
-            hipLaunchKernelGGL(beam_router_logits_small<float>, grid, dim3(256), 0, st,
-                               (const float*)a.x, a.w, part, T, H, E, H / nsplit);
+        const int ks = H / nsplit;   // <= 4096 (small_splits), a multiple of 4
+        const int nit = (ks + 1023) / 1024;
+        auto go = [&](auto nitc, auto tbc) {
+            constexpr int NIT = decltype(nitc)::value, TB = decltype(tbc)::value;
+            if (a.x_bf16)
+                hipLaunchKernelGGL((beam_router_logits_small<uint16_t, NIT, TB>), grid, dim3(256), 0, st,
+                                   (const uint16_t*)a.x, a.w, part, T, H, E, ks);
+            else
+                hipLaunchKernelGGL((beam_router_logits_small<float, NIT, TB>), grid, dim3(256), 0, st,
+                                   (const float*)a.x, a.w, part, T, H, E, ks);
+        };
+        auto go_nit = [&](auto tbc) {
+            if (nit <= 1) go(std::integral_constant<int, 1>{}, tbc);
+            else if (nit <= 2) go(std::integral_constant<int, 2>{}, tbc);
+            else go(std::integral_constant<int, 4>{}, tbc);
+        };
+        if (T <= 8) go_nit(std::integral_constant<int, 8>{});
+        else go_nit(std::integral_constant<int, kSmallT>{});
     } else if (route_uses_mfma(T, E, a.x_bf16)) {
         dim3 grid((T + kMT - 1) / kMT, E / kME, nsplit);
         hipLaunchKernelGGL(beam_router_logits_mfma, grid, dim3(256), 0, st, (const uint16_t*)a.x, a.w,
