@@ -58,7 +58,10 @@ def ridge_rows(w_dtype):
 SIDE_STREAM_MIN_T = 1024          # tokens from which the input quantisation gets its own stream
 RIDGE_ROWS = 312.5               # rows per expert where weight streaming stops bounding (bf16 and fp8)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-EXPERTS_SRC = os.path.join(ROOT, "expert_routed_ffn_amd", "csrc", "experts.hip")
+# the sources of every kernel inside the experts and dense MLP calls (the
+# GEMMs, work items, SwiGLU slices, e4m3 and MXFP4 re-quantisation of a)
+EXPERTS_SRCS = [os.path.join(ROOT, "expert_routed_ffn_amd", "csrc", f)
+                for f in ("experts.hip", "common.h", "mx.hip")]
 DEFAULT_CONFIGS = ("skew_t64,prefill_t2048,prefill_fp8_t16384,prefill_bf16_t16384,"
                    "decode_t8_mxfp4,skew_t64_mxfp4,prefill_mxfp4_t16384,dense_t8,dense_t2048,ep8_shard_t8,"
                    "ep8_shard_t2048")
@@ -148,7 +151,10 @@ class HipEvents:
 
 
 def kernel_hash():
-    return hashlib.sha256(open(EXPERTS_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in EXPERTS_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def lcfg(wl):
@@ -315,7 +321,7 @@ def algorithmic(wl, D):
 def traffic_for(workload, call="experts"):
     """Measured HBM bytes per beam_moe_experts (or beam_moe_dense_mlp) call
     from the committed rocprofv3 counter summary, or None if it is missing
-    or was taken on a different expert-kernel source."""
+    or was taken on different sources of the call's kernels."""
     try:
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):

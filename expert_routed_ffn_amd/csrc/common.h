@@ -128,54 +128,33 @@ BEAM_DEV float silu_f32(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __exp
 
 namespace beam {
 
-// Dynamic per-row e4m3 quantisation of `n` values read through `load(i)`
-// (n <= 8 * 1024, n % 4 == 0) by one 256-thread workgroup:
+// Dynamic per-row e4m3 quantisation of `n` values (n % 4 == 0) by one
+// wave, with no barriers:
 //   scale = amax / 448 (correctly rounded fp32; 1 for an all-zero row),
 //   code  = e4m3(v / scale) with a correctly rounded fp32 division.
-constexpr int kQuantMaxIter = 8;
-template <typename Load4>
-BEAM_DEV void quantize_row_e4m3(Load4 load4, int n, uint8_t* __restrict__ q, float* scale_out,
-                                float* red) {
-    float v[kQuantMaxIter][4];
-    float amax = 0.f;
-#pragma unroll
-    for (int it = 0; it < kQuantMaxIter; ++it) {
-        const int i = (it * 256 + threadIdx.x) * 4;
-        if (i < n) {
-            const float4 f = load4(i);
-            v[it][0] = f.x; v[it][1] = f.y; v[it][2] = f.z; v[it][3] = f.w;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(v[it][j]));
-        }
-    }
-    amax = block_max<4>(amax, red);
-    const float s = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
-#pragma unroll
-    for (int it = 0; it < kQuantMaxIter; ++it) {
-        const int i = (it * 256 + threadIdx.x) * 4;
-        if (i < n) {
-            *reinterpret_cast<uint32_t*>(q + i) = e4m3x4(__fdiv_rn(v[it][0], s), __fdiv_rn(v[it][1], s),
-                                                         __fdiv_rn(v[it][2], s), __fdiv_rn(v[it][3], s));
-        }
-    }
-    if (threadIdx.x == 0) *scale_out = s;
-}
-
-// The same quantisation of one row by one wave (no barriers): lane l holds
-// the 4-element chunks l, l + 64, ...; NIT >= n / 256 chunks per lane.  The
-// row maximum is exact whatever the reduction order, so the codes and the
-// scale equal those of quantize_row_e4m3.
-template <int NIT, typename Load4>
-BEAM_DEV void quantize_row_e4m3_wave(Load4 load4, int n, uint8_t* __restrict__ q, float* scale_out) {
+// Lane l holds the 4-element chunks l, l + 64, ...; NIT >= n / 256 chunks
+// per lane.  `load_raw(i)` loads chunk i as stored and `widen` turns it into
+// fp32; all NIT loads are issued before the first is widened (lanes past n
+// re-read chunk 0 and drop it), so a lane's loads cost one memory round
+// trip.  The row maximum is exact whatever the reduction order.
+template <int NIT, typename LoadRaw, typename Widen>
+BEAM_DEV void quantize_row_e4m3_wave(LoadRaw load_raw, Widen widen, int n, uint8_t* __restrict__ q,
+                                     float* scale_out) {
     const int lane = threadIdx.x & 63;
+    decltype(load_raw(0)) raw[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int i = (it * 64 + lane) * 4;
+        raw[it] = load_raw(i < n ? i : 0);
+    }
     float v[NIT][4];
     float amax = 0.f;
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
         const int i = (it * 64 + lane) * 4;
+        const float4 f = widen(raw[it]);
+        v[it][0] = f.x; v[it][1] = f.y; v[it][2] = f.z; v[it][3] = f.w;
         if (i < n) {
-            const float4 f = load4(i);
-            v[it][0] = f.x; v[it][1] = f.y; v[it][2] = f.z; v[it][3] = f.w;
 #pragma unroll
             for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(v[it][j]));
         }

@@ -709,16 +709,23 @@ BEAM_DEV void gemm_item_wide(const GemmParams& p, int e, int row0, int rows, int
     if constexpr (MX) {
         // two threads per item row, each copying every other 16-code chunk
         // of the row's whole K (nk <= 16: K <= 8192): one row-map load, then
-        // up to eight independent loads (a loop over all 128 x nk chunks
-        // made each thread wait on five row-map / code load pairs in turn)
+        // up to eight independent loads, all issued before the first LDS
+        // store (a store next to its load would wait for it before the
+        // next load goes out)
         const int rr = threadIdx.x >> 1, c0 = threadIdx.x & 1;
         const int src = rr < rows ? rr : 0;
         const size_t srow_mx = G1 ? (size_t)p.row_token[row0 + src] : (size_t)(row0 + src);
         const uint8_t* pmx = p.mx_act + srow_mx * kblk;
+        uint4 sv[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int c = c0 + 2 * i;
-            if (c < nk) ssc[rr * 16 + c] = ld16(pmx + c * 16);
+            sv[i] = c < nk ? ld16(pmx + c * 16) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int c = c0 + 2 * i;
+            if (c < nk) ssc[rr * 16 + c] = sv[i];
         }
         const size_t wrow0 = (size_t)e * (G1 ? 2 * p.F : p.H);
 #pragma unroll
@@ -1039,8 +1046,9 @@ __global__ __launch_bounds__(256) void beam_quantize_a_e4m3(const float* __restr
     const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= (size_t)offsets[E]) return;   // whole wave exits together
     const float* ar = a + row * F;
-    auto load4 = [&](int i) { return *reinterpret_cast<const float4*>(ar + i); };
-    quantize_row_e4m3_wave<NIT>(load4, F, aq + row * F, ascale + row);
+    auto load_raw = [&](int i) { return *reinterpret_cast<const float4*>(ar + i); };
+    auto widen = [](float4 f) { return f; };
+    quantize_row_e4m3_wave<NIT>(load_raw, widen, F, aq + row * F, ascale + row);
 }
 
 // SwiGLU of K-split GEMM1 sums: a[r][f] = bf16(silu(sum_s g) * sum_s v), the

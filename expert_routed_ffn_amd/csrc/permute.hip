@@ -140,12 +140,12 @@ __global__ __launch_bounds__(256) void beam_quantize_x_e4m3(
     const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= (size_t)T) return;   // whole wave exits together
     const uint16_t* xr = x + row * H;
-    auto load4 = [&](int i) {
-        const uint2 u = *reinterpret_cast<const uint2*>(xr + i);
+    auto load_raw = [&](int i) { return *reinterpret_cast<const uint2*>(xr + i); };   // 4 bf16
+    auto widen = [](uint2 u) {
         return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
                            __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
     };
-    quantize_row_e4m3_wave<NIT>(load4, H, xq + row * H, xscale + row);
+    quantize_row_e4m3_wave<NIT>(load_raw, widen, H, xq + row * H, xscale + row);
 }
 
 static int n_chunks(int TK) { return (TK + kPermChunk - 1) / kPermChunk; }
