@@ -310,6 +310,32 @@ __global__ __launch_bounds__(256) void beam_router_logits_mfma(
 // ---------------------------------------------------------------------------
 constexpr int kMaxTopn = 4;
 
+// 64-bit value of the lane given by the DPP control CTRL (a permutation
+// inside each row of 16 lanes; every lane is active)
+template <int CTRL> BEAM_DEV uint64_t dpp_u64(uint64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+    return ((uint64_t)hi << 32) | lo;
+}
+BEAM_DEV uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+BEAM_DEV uint64_t readlane_u64(uint64_t v, int l) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+// Maximum over the wave, the same in every lane: within each row of 16
+// lanes by four DPP exchanges (swap neighbours, swap pairs, mirror halves
+// of 8, mirror the row), then the four row maxima read as scalars.  No LDS
+// round trips, unlike a butterfly of lane shuffles.
+BEAM_DEV uint64_t wave_max_u64(uint64_t v) {
+    v = max_u64(v, dpp_u64<0xB1>(v));    // quad_perm [1,0,3,2]
+    v = max_u64(v, dpp_u64<0x4E>(v));    // quad_perm [2,3,0,1]
+    v = max_u64(v, dpp_u64<0x141>(v));   // row_half_mirror
+    v = max_u64(v, dpp_u64<0x140>(v));   // row_mirror
+    return max_u64(max_u64(readlane_u64(v, 0), readlane_u64(v, 16)),
+                   max_u64(readlane_u64(v, 32), readlane_u64(v, 48)));
+}
+
 template <int EPL>
 __global__ __launch_bounds__(256) void beam_route_select(
     const float* __restrict__ part, int nsplit, float* __restrict__ logits_out,
@@ -401,7 +427,7 @@ __global__ __launch_bounds__(256) void beam_route_select(
     const int my_group = lane / lpg;
     int rank = 0;
     for (int g = 0; g < G; ++g) {
-        const float o = __shfl(gs, g * lpg, kWave);
+        const float o = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gs), g * lpg));
         rank += (o > gs) || (o == gs && g < my_group);
     }
     const bool group_kept = (my_group < G) && (rank < kg);
@@ -422,18 +448,14 @@ __global__ __launch_bounds__(256) void beam_route_select(
         uint64_t best = 0;
 #pragma unroll
         for (int i = 0; i < EPL; ++i) best = key[i] > best ? key[i] : best;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const uint64_t other = __shfl_xor(best, o, kWave);
-            best = other > best ? other : best;
-        }
+        best = wave_max_u64(best);
         const int e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
         const int owner = e / EPL, slot = e - owner * EPL;
         float se = 0.f;
 #pragma unroll
         for (int i = 0; i < EPL; ++i)
             if (i == slot) se = s[i];
-        se = __shfl(se, owner, kWave);
+        se = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(se), owner));
         if (lane == owner) {
 #pragma unroll
             for (int i = 0; i < EPL; ++i)
