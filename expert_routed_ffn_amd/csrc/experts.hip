@@ -504,12 +504,38 @@ BEAM_DEV void gemm_item_lds(const GemmParams& p, int e, int row0, int rows, int 
         step(IC<0>{}, IC<0>{}, kit);
     }
 
+    if constexpr (KIND == W_FP8) {
+        // every scale the row blocks need is loaded before the first store
+        // (a store between them would make each block wait for its own)
+        float sa[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const int c = nb * 16 + r;
-        if (c < rows) {
-            const int tok = G1 ? p.row_token[row0 + c] : row0 + c;
-            store_block<KIND, G1>(p, e, a0, a1, (size_t)row0 + c, tok, acc0[nb], acc1[nb]);
+        for (int nb = 0; nb < NB; ++nb) {
+            const int c = nb * 16 + r < rows ? nb * 16 + r : 0;
+            sa[nb] = G1 ? p.act_scale[p.row_token[row0 + c]] : p.act_scale[row0 + c];
+        }
+        const size_t wrow0 = (size_t)e * (G1 ? 2 * p.F : p.H);
+        const float4 sw0 = *reinterpret_cast<const float4*>(p.wscale + wrow0 + a0 + 4 * g);
+        const float4 sw1 = *reinterpret_cast<const float4*>(p.wscale + wrow0 + a1 + 4 * g);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int c = nb * 16 + r;
+            if (c < rows) {
+                if constexpr (G1) {   // a1 = F + a0: the up rows of the gate rows a0
+                    store_swiglu_s<KIND>(p, a0 + 4 * g, (size_t)row0 + c, sa[nb], sw0, sw1, acc0[nb], acc1[nb]);
+                } else {
+                    store_out_s<KIND>(p, a0 + 4 * g, (size_t)row0 + c, sa[nb], sw0, acc0[nb]);
+                    store_out_s<KIND>(p, a1 + 4 * g, (size_t)row0 + c, sa[nb], sw1, acc1[nb]);
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int c = nb * 16 + r;
+            if (c < rows) {
+                const int tok = G1 ? p.row_token[row0 + c] : row0 + c;
+                store_block<KIND, G1>(p, e, a0, a1, (size_t)row0 + c, tok, acc0[nb], acc1[nb]);
+            }
         }
     }
 }
