@@ -4,6 +4,7 @@ quantisation, grouped experts (fp32, bf16, fp8) and combine + norm.  Sizes
 span several tiles with ragged tails; edge cases include single tokens,
 zero-token experts and every token on one expert."""
 
+import dataclasses
 import math
 
 import numpy as np
@@ -33,8 +34,23 @@ def lcfg(wl):
     ("prefill_fp8_t16384", 16384),
 ])
 def test_route_parity(wname, T):
-    wl = synth.WORKLOADS[wname]
     say(f"route {wname} T={T}")
+    _check_route(synth.WORKLOADS[wname], T)
+
+
+# The small-batch router (T <= 16) is compiled per chunk count of its K
+# slice (1, 2 or 4 chunks of 1024 per thread) and per token batch (8 or
+# 16): hidden sizes and token counts that reach each variant, bf16 and fp32.
+@pytest.mark.parametrize("wname,H,T", [
+    ("decode_t8", 2048, 3), ("decode_t8", 3840, 12), ("decode_t8", 4096, 9), ("decode_t8", 7936, 16),
+    ("tiny_fp32", 3840, 5), ("tiny_fp32", 1024, 16), ("tiny_fp32", 4352, 11),
+])
+def test_route_small_batch_shapes(wname, H, T):
+    say(f"route {wname} H={H} T={T}")
+    _check_route(dataclasses.replace(synth.WORKLOADS[wname], hidden=H), T)
+
+
+def _check_route(wl, T):
     cfg = lcfg(wl)
     w_r, bias = synth.make_router(wl, DEV)
     x, _, _, _ = synth.make_activations(wl, DEV, T=T)
