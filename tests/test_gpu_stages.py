@@ -136,16 +136,19 @@ def test_permute_every_token_on_one_expert():
     assert np.array_equal(off, o_off) and np.array_equal(rt, o_rt) and np.array_equal(pr, o_pr)
 
 
-def test_quantize_x_e4m3_bit_exact():
-    say("per-token e4m3 quantisation")
-    T, H = 37, 5120
+# hidden sizes that fill the quantiser's chunks exactly (5120) or leave
+# lanes past the row (1280, 3328)
+@pytest.mark.parametrize("H", [5120, 1280, 3328])
+def test_quantize_x_e4m3_bit_exact(H):
+    say(f"per-token e4m3 quantisation H={H}")
+    T = 37
     g = torch.Generator(device=DEV).manual_seed(3)
     scale = torch.logspace(-3, 3, T, device=DEV).unsqueeze(1)
     x = (torch.randn((T, H), generator=g, device=DEV) * scale)
     x[5] = 0.0                                           # all-zero row
     x[6] = x[6] * torch.logspace(-6, 0, H, device=DEV)   # wide dynamic range -> e4m3 subnormals
     x = x.to(torch.bfloat16)
-    cfg = beam.LayerCfg()
+    cfg = beam.LayerCfg(hidden=H)
     ids = torch.zeros((T, cfg.topk), dtype=torch.int32, device=DEV) + torch.arange(cfg.topk, dtype=torch.int32, device=DEV)
     off = torch.empty(cfg.n_experts + 1, dtype=torch.int32, device=DEV)
     rt = torch.empty(T * cfg.topk, dtype=torch.int32, device=DEV)
@@ -433,10 +436,14 @@ def test_pack_layout(w_dtype):
     (256, 4, 4, torch.float32, "f32", 5),
     (5120, 8, 300, torch.float32, "bf16", 20),     # more tokens: one row at a time
     (5120, 8, 300, torch.bfloat16, "bf16", 20),
+    # rows that end part-way through a thread's chunks, on both load paths
+    (1280, 8, 300, torch.bfloat16, "bf16", 20),
+    (1280, 8, 300, torch.float32, "f32", 7),
+    (3328, 6, 5, torch.float32, "bf16", 3),
 ])
 def test_combine_norm_parity(H, K, T, y_dtype, act, n):
     say(f"combine_norm H={H} K={K} T={T} y={y_dtype} act={act} n={n}")
-    cfg = beam.LayerCfg(hidden=H, topk=K) if H == 5120 else beam.LayerCfg(256, 16, 4, 2, K, 2, 128)
+    cfg = beam.LayerCfg(hidden=H, topk=K) if H != 256 else beam.LayerCfg(256, 16, 4, 2, K, 2, 128)
     g = torch.Generator(device=DEV).manual_seed(21)
     TK = T * K
     adt = torch.bfloat16 if act == "bf16" else torch.float32
