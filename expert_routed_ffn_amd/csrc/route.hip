@@ -203,14 +203,14 @@ __global__ __launch_bounds__(256) void beam_router_logits_tiled(
 // so every product x*hi, x*mid, x*lo of a bf16 activation is exact in fp32
 // and the bf16 MFMA accumulates them in fp32 -- the pages' exact three-way
 // bf16 decomposition of the FP32 router for large batches.
-// Workgroup tile: 64 tokens x 64 experts; each wave owns 16 experts and all
-// four 16-token blocks.  K is split over gridDim.z slices (deterministic
+// Workgroup tile: 128 tokens x 64 experts; each wave owns 16 experts and all
+// eight 16-token blocks, so every split weight fragment feeds eight MFMAs.  K is split over gridDim.z slices (deterministic
 // partial sums, added in slice order by the selection kernel) so small
 // batches still fill the chip.  Operands are staged through LDS (rows
 // padded to 80 bytes: conflict-free 16-byte fragment reads), double-buffered
 // in steps of 32 along K.
 // ---------------------------------------------------------------------------
-constexpr int kMT = 64, kME = 64, kMK = 32;
+constexpr int kMT = 128, kME = 64, kMK = 32;
 
 BEAM_DEV void split3_bf16(float v, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
     const uint32_t u = __float_as_uint(v);
@@ -232,20 +232,24 @@ __global__ __launch_bounds__(256) void beam_router_logits_mfma(
     const int kbeg = sl * kchunk, nk = kchunk / kMK;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
-    // loader role: row lr (token / expert of the tile), 8-element chunk lc
+    // loader role: rows lr and lr + 64 of the token tile and row lr of the
+    // expert tile, 8-element chunk lc
     const int lr = tid >> 2, lc = tid & 3;
-    const bool tv = t0 + lr < T;
-    const uint16_t* xp = x + (size_t)(tv ? t0 + lr : 0) * H + kbeg + 8 * lc;
+    const bool tv0 = t0 + lr < T, tv1 = t0 + 64 + lr < T;
+    const uint16_t* xp0 = x + (size_t)(tv0 ? t0 + lr : 0) * H + kbeg + 8 * lc;
+    const uint16_t* xp1 = x + (size_t)(tv1 ? t0 + 64 + lr : 0) * H + kbeg + 8 * lc;
     const float* wp = w + (size_t)(e0 + lr) * H + kbeg + 8 * lc;
-    uint4 xr;
+    uint4 xr0, xr1;
     float4 w0, w1;
     auto gload = [&](int kk) {
-        xr = tv ? *reinterpret_cast<const uint4*>(xp + kk) : make_uint4(0, 0, 0, 0);
+        xr0 = tv0 ? *reinterpret_cast<const uint4*>(xp0 + kk) : make_uint4(0, 0, 0, 0);
+        xr1 = tv1 ? *reinterpret_cast<const uint4*>(xp1 + kk) : make_uint4(0, 0, 0, 0);
         w0 = *reinterpret_cast<const float4*>(wp + kk);
         w1 = *reinterpret_cast<const float4*>(wp + kk + 4);
     };
     auto swrite = [&](int buf) {
-        xs[buf][lr][lc] = xr;
+        xs[buf][lr][lc] = xr0;
+        xs[buf][64 + lr][lc] = xr1;
         const float v[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
         uint32_t hp[4], mp[4], lp[4];
 #pragma unroll
@@ -262,9 +266,9 @@ __global__ __launch_bounds__(256) void beam_router_logits_mfma(
         wsh[buf][2][lr][lc] = make_uint4(lp[0], lp[1], lp[2], lp[3]);
     };
 
-    f32x4 acc[4];
+    f32x4 acc[kMT / 16];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < kMT / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     gload(0);
     swrite(0);
     __syncthreads();
@@ -276,7 +280,7 @@ __global__ __launch_bounds__(256) void beam_router_logits_mfma(
 #pragma unroll
         for (int pl = 0; pl < 3; ++pl) a[pl] = __builtin_bit_cast(bf16x8, wsh[cur][pl][wave * 16 + r][g]);
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
+        for (int nb = 0; nb < kMT / 16; ++nb) {
             const bf16x8 b = __builtin_bit_cast(bf16x8, xs[cur][nb * 16 + r][g]);
             // small terms first
             acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], b, acc[nb], 0, 0, 0);
@@ -289,7 +293,7 @@ __global__ __launch_bounds__(256) void beam_router_logits_mfma(
     // lane holds D[4g+i][r] = expert e0 + 16*wave + 4g + i, token t0 + 16*nb + r
     float* out = part + (size_t)sl * T * E;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
+    for (int nb = 0; nb < kMT / 16; ++nb) {
         const int t = t0 + nb * 16 + r;
         if (t < T)
             *reinterpret_cast<float4*>(out + (size_t)t * E + e0 + wave * 16 + 4 * g) =

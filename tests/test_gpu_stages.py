@@ -31,7 +31,7 @@ def lcfg(wl):
     ("tiny_fp32", 1), ("tiny_fp32", 4), ("tiny_fp32", 33),
     ("decode_t8", 1), ("decode_t8", 8), ("decode_t8", 16), ("decode_t8", 17),
     ("skew_t64", 64), ("decode_t8", 300), ("prefill_t2048", 2048), ("decode_t8", 100),
-    ("prefill_fp8_t16384", 16384),
+    ("prefill_fp8_t16384", 16384), ("decode_t8", 512), ("decode_t8", 700),
 ])
 def test_route_parity(wname, T):
     say(f"route {wname} T={T}")
@@ -48,6 +48,16 @@ def test_route_parity(wname, T):
 def test_route_small_batch_shapes(wname, H, T):
     say(f"route {wname} H={H} T={T}")
     _check_route(dataclasses.replace(synth.WORKLOADS[wname], hidden=H), T)
+
+
+# The matrix-core router cuts K into as many slices as fill the chip (each a
+# multiple of 32 values that divides H, at least 256): hidden sizes whose
+# slice counts differ (9 slices of 256 at H=2304 and T=600, 5 at H=1280 and
+# T=1000, 1 at T=16384 above) with ragged token tiles.
+@pytest.mark.parametrize("H,T", [(2304, 600), (1280, 1000), (5120, 1500)])
+def test_route_split_k_shapes(H, T):
+    say(f"route split-K H={H} T={T}")
+    _check_route(dataclasses.replace(synth.WORKLOADS["decode_t8"], hidden=H), T)
 
 
 def _check_route(wl, T):
