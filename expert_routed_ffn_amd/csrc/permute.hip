@@ -11,7 +11,12 @@
 namespace beam {
 
 constexpr int kPermThreads = 256;
-constexpr int kPermChunk = 4096;   // pairs per workgroup in the multi-block path
+constexpr int kPermFused = 4096;   // pairs up to which one workgroup does the whole permutation
+// pairs per workgroup in the multi-block path: 1024 up to 32768 pairs (the
+// scatter of a chunk is serial over its 256-pair steps, so smaller chunks
+// spread it over more workgroups), 4096 above (the one-workgroup scan walks
+// every chunk's histogram in turn)
+static int perm_chunk(int TK) { return TK <= 32768 ? 1024 : 4096; }
 constexpr int kMaxE = 256;
 
 // Stable scatter of pairs [begin, end) given per-expert cursors in LDS
@@ -53,7 +58,7 @@ BEAM_DEV void stable_scatter(const int32_t* __restrict__ ids, int e_base, int be
     }
 }
 
-// Whole permutation in one workgroup (T*K <= kPermChunk).
+// Whole permutation in one workgroup (T*K <= kPermFused).
 __global__ __launch_bounds__(kPermThreads) void beam_permute_fused(
     const int32_t* __restrict__ ids, int e_base, int TK, int K, int E, int ebits,
     int32_t* __restrict__ offsets, int32_t* __restrict__ row_token, int32_t* __restrict__ pair_row) {
@@ -81,13 +86,13 @@ __global__ __launch_bounds__(kPermThreads) void beam_permute_fused(
 
 // Multi-block path, step 1: per-chunk histograms bh[b][e].
 __global__ __launch_bounds__(kPermThreads) void beam_permute_hist(
-    const int32_t* __restrict__ ids, int e_base, int TK, int E, int32_t* __restrict__ bh) {
+    const int32_t* __restrict__ ids, int e_base, int TK, int E, int chunk, int32_t* __restrict__ bh) {
     __shared__ int hist[kMaxE];
     const int tid = threadIdx.x;
     if (tid < E) hist[tid] = 0;
     __syncthreads();
-    const int begin = blockIdx.x * kPermChunk;
-    const int end = min(begin + kPermChunk, TK);
+    const int begin = blockIdx.x * chunk;
+    const int end = min(begin + chunk, TK);
     for (int p = begin + tid; p < end; p += kPermThreads) {
         const int e = ids[p] - e_base;
         if ((unsigned)e < (unsigned)E) atomicAdd(&hist[e], 1);
@@ -120,15 +125,15 @@ __global__ __launch_bounds__(kPermThreads) void beam_permute_scan(
 
 // Step 3: stable scatter of each chunk from its per-expert base rows.
 __global__ __launch_bounds__(kPermThreads) void beam_permute_scatter(
-    const int32_t* __restrict__ ids, int e_base, int TK, int K, int E, int ebits,
+    const int32_t* __restrict__ ids, int e_base, int TK, int K, int E, int ebits, int chunk,
     const int32_t* __restrict__ bbase, int32_t* __restrict__ row_token,
     int32_t* __restrict__ pair_row) {
     __shared__ int cursor[kMaxE];
     const int tid = threadIdx.x;
     if (tid < E) cursor[tid] = bbase[(size_t)blockIdx.x * E + tid];
     __syncthreads();
-    const int begin = blockIdx.x * kPermChunk;
-    const int end = min(begin + kPermChunk, TK);
+    const int begin = blockIdx.x * chunk;
+    const int end = min(begin + chunk, TK);
     stable_scatter(ids, e_base, begin, end, K, E, ebits, cursor, row_token, pair_row);
 }
 
@@ -148,7 +153,7 @@ __global__ __launch_bounds__(256) void beam_quantize_x_e4m3(
     quantize_row_e4m3_wave<NIT>(load_raw, widen, H, xq + row * H, xscale + row);
 }
 
-static int n_chunks(int TK) { return (TK + kPermChunk - 1) / kPermChunk; }
+static int n_chunks(int TK) { return TK <= kPermFused ? 1 : (TK + perm_chunk(TK) - 1) / perm_chunk(TK); }
 
 size_t permute_ws_bytes(int T, int K, int E) {
     const int nb = n_chunks(T * K);
@@ -166,11 +171,13 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t st) {
     } else {
         int32_t* bh = static_cast<int32_t*>(a.ws);
         int32_t* bb = bh + (size_t)nb * a.E;
-        hipLaunchKernelGGL(beam_permute_hist, dim3(nb), dim3(kPermThreads), 0, st, a.ids, a.e_base, TK, a.E, bh);
+        const int chunk = perm_chunk(TK);
+        hipLaunchKernelGGL(beam_permute_hist, dim3(nb), dim3(kPermThreads), 0, st, a.ids, a.e_base, TK, a.E,
+                           chunk, bh);
         hipLaunchKernelGGL(beam_permute_scan, dim3(1), dim3(kPermThreads), 0, st, bh, nb, TK, a.E,
                            a.offsets, bb);
         hipLaunchKernelGGL(beam_permute_scatter, dim3(nb), dim3(kPermThreads), 0, st, a.ids, a.e_base, TK, a.K,
-                           a.E, ebits, bb, a.row_token, a.pair_row);
+                           a.E, ebits, chunk, bb, a.row_token, a.pair_row);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || a.xq == nullptr) return err;
