@@ -107,17 +107,34 @@ __global__ __launch_bounds__(kPermThreads) void beam_permute_scan(
     int32_t* __restrict__ bbase) {
     __shared__ int tmp[4];
     const int e = threadIdx.x;
+    // the chunks' counts of expert e, kScanBatch loads in flight at a time
+    // (indices past the last chunk re-read it and count zero)
+    constexpr int kScanBatch = 8;
+    const int ec = e < E ? e : 0;
+    auto load_batch = [&](int b0, int (&v)[kScanBatch]) {
+#pragma unroll
+        for (int j = 0; j < kScanBatch; ++j) v[j] = bh[(size_t)min(b0 + j, nb - 1) * E + ec];
+#pragma unroll
+        for (int j = 0; j < kScanBatch; ++j) v[j] = b0 + j < nb ? v[j] : 0;
+    };
     int tot = 0;
-    if (e < E)
-        for (int b = 0; b < nb; ++b) tot += bh[(size_t)b * E + e];
+    for (int b0 = 0; b0 < nb; b0 += kScanBatch) {
+        int v[kScanBatch];
+        load_batch(b0, v);
+#pragma unroll
+        for (int j = 0; j < kScanBatch; ++j) tot += v[j];
+    }
     int total;
     const int excl = block_exclusive_scan(e < E ? tot : 0, tmp, &total);
-    if (e < E) {
-        offsets[e] = excl;
-        int run = excl;
-        for (int b = 0; b < nb; ++b) {
-            bbase[(size_t)b * E + e] = run;
-            run += bh[(size_t)b * E + e];
+    if (e < E) offsets[e] = excl;
+    int run = excl;
+    for (int b0 = 0; b0 < nb; b0 += kScanBatch) {
+        int v[kScanBatch];
+        load_batch(b0, v);
+#pragma unroll
+        for (int j = 0; j < kScanBatch; ++j) {
+            if (e < E && b0 + j < nb) bbase[(size_t)(b0 + j) * E + e] = run;
+            run += v[j];
         }
     }
     if (e == 0) offsets[E] = total;
