@@ -203,14 +203,18 @@ __global__ __launch_bounds__(256) void beam_router_logits_tiled(
 // so every product x*hi, x*mid, x*lo of a bf16 activation is exact in fp32
 // and the bf16 MFMA accumulates them in fp32 -- the pages' exact three-way
 // bf16 decomposition of the FP32 router for large batches.
-// Workgroup tile: 128 tokens x 64 experts; each wave owns 16 experts and all
-// eight 16-token blocks, so every split weight fragment feeds eight MFMAs.  K is split over gridDim.z slices (deterministic
+// Workgroup tile: 128 tokens x ME experts over 4*ME threads; each wave owns
+// 16 experts and all eight 16-token blocks, so every split weight fragment
+// feeds eight MFMAs.  ME = 128 (512 threads, 80 KB of LDS) from 1024 tokens
+// halves the weight-tile re-reads; below, ME = 64 keeps twice as many
+// workgroups for the small grids.  K is split over gridDim.z slices (deterministic
 // partial sums, added in slice order by the selection kernel) so small
 // batches still fill the chip.  Operands are staged through LDS (rows
 // padded to 80 bytes: conflict-free 16-byte fragment reads), double-buffered
 // in steps of 32 along K.
 // ---------------------------------------------------------------------------
-constexpr int kMT = 128, kME = 64, kMK = 32;
+constexpr int kMT = 128, kME = 64, kMK = 32;   // kME: the expert tile's granularity
+constexpr int kMEWideT = 1024;                  // tokens from which the expert tile is 2 * kME
 
 BEAM_DEV void split3_bf16(float v, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
     const uint32_t u = __float_as_uint(v);
@@ -223,33 +227,40 @@ BEAM_DEV void split3_bf16(float v, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
     lo = __float_as_uint(r2) >> 16;
 }
 
-__global__ __launch_bounds__(256) void beam_router_logits_mfma(
+template <int ME>
+__global__ __launch_bounds__(4 * ME) void beam_router_logits_mfma(
     const uint16_t* __restrict__ x, const float* __restrict__ w, float* __restrict__ part,
     int T, int H, int E, int kchunk) {
     __shared__ uint4 xs[2][kMT][5];
-    __shared__ uint4 wsh[2][3][kME][5];
-    const int t0 = blockIdx.x * kMT, e0 = blockIdx.y * kME, sl = blockIdx.z;
+    __shared__ uint4 wsh[2][3][ME][5];
+    const int t0 = blockIdx.x * kMT, e0 = blockIdx.y * ME, sl = blockIdx.z;
     const int kbeg = sl * kchunk, nk = kchunk / kMK;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
-    // loader role: rows lr and lr + 64 of the token tile and row lr of the
+    // loader role: rows lr + ME * j of the token tile and row lr of the
     // expert tile, 8-element chunk lc
+    constexpr int XJ = kMT / ME;
     const int lr = tid >> 2, lc = tid & 3;
-    const bool tv0 = t0 + lr < T, tv1 = t0 + 64 + lr < T;
-    const uint16_t* xp0 = x + (size_t)(tv0 ? t0 + lr : 0) * H + kbeg + 8 * lc;
-    const uint16_t* xp1 = x + (size_t)(tv1 ? t0 + 64 + lr : 0) * H + kbeg + 8 * lc;
+    bool tv[XJ];
+    const uint16_t* xp[XJ];
+#pragma unroll
+    for (int j = 0; j < XJ; ++j) {
+        tv[j] = t0 + ME * j + lr < T;
+        xp[j] = x + (size_t)(tv[j] ? t0 + ME * j + lr : 0) * H + kbeg + 8 * lc;
+    }
     const float* wp = w + (size_t)(e0 + lr) * H + kbeg + 8 * lc;
-    uint4 xr0, xr1;
+    uint4 xr[XJ];
     float4 w0, w1;
     auto gload = [&](int kk) {
-        xr0 = tv0 ? *reinterpret_cast<const uint4*>(xp0 + kk) : make_uint4(0, 0, 0, 0);
-        xr1 = tv1 ? *reinterpret_cast<const uint4*>(xp1 + kk) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < XJ; ++j)
+            xr[j] = tv[j] ? *reinterpret_cast<const uint4*>(xp[j] + kk) : make_uint4(0, 0, 0, 0);
         w0 = *reinterpret_cast<const float4*>(wp + kk);
         w1 = *reinterpret_cast<const float4*>(wp + kk + 4);
     };
     auto swrite = [&](int buf) {
-        xs[buf][lr][lc] = xr0;
-        xs[buf][64 + lr][lc] = xr1;
+#pragma unroll
+        for (int j = 0; j < XJ; ++j) xs[buf][ME * j + lr][lc] = xr[j];
         const float v[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
         uint32_t hp[4], mp[4], lp[4];
 #pragma unroll
@@ -477,12 +488,19 @@ __global__ __launch_bounds__(256) void beam_route_select(
 int route_epl(int E) { return E <= 64 ? 1 : (E <= 128 ? 2 : 4); }
 
 
+// Expert tile of the matrix-core router for T tokens.
+static int route_me(int T, int E) { return (T >= kMEWideT && E % (2 * kME) == 0) ? 2 * kME : kME; }
+
 // K slices of the matrix-core router for T tokens: enough workgroups to
-// fill the chip, each slice a multiple of 32 that divides H, at least 256.
+// fill the chip (about 640 with the 64-expert tile, three per CU; 256 with
+// the 128-expert tile, whose 80 KB of LDS leave one or two per CU), each
+// slice a multiple of 32 that divides H, at least 256.
 int route_splits(int T, int H, int E) {
     if (T <= 0 || E % kME != 0) return 1;   // only the matrix-core router splits K
-    const int tiles = ((T + kMT - 1) / kMT) * (E / kME);
-    int want = (640 + tiles - 1) / tiles;
+    const int me = route_me(T, E);
+    const int tiles = ((T + kMT - 1) / kMT) * (E / me);
+    const int target = me == kME ? 640 : 256;
+    int want = (target + tiles - 1) / tiles;
     const int steps = H / kMK;
     if (want > H / 256) want = H / 256;
     for (int sl = want; sl > 1; --sl)
@@ -533,9 +551,14 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
         if (T <= 8) go_nit(std::integral_constant<int, 8>{});
         else go_nit(std::integral_constant<int, kSmallT>{});
     } else if (route_uses_mfma(T, E, a.x_bf16)) {
-        dim3 grid((T + kMT - 1) / kMT, E / kME, nsplit);
-        hipLaunchKernelGGL(beam_router_logits_mfma, grid, dim3(256), 0, st, (const uint16_t*)a.x, a.w,
-                           part, T, H, E, H / nsplit);
+        const int me = route_me(T, E);
+        dim3 grid((T + kMT - 1) / kMT, E / me, nsplit);
+        if (me == kME)
+            hipLaunchKernelGGL(beam_router_logits_mfma<kME>, grid, dim3(4 * kME), 0, st, (const uint16_t*)a.x, a.w,
+                               part, T, H, E, H / nsplit);
+        else
+            hipLaunchKernelGGL(beam_router_logits_mfma<2 * kME>, grid, dim3(8 * kME), 0, st, (const uint16_t*)a.x,
+                               a.w, part, T, H, E, H / nsplit);
     } else {
         dim3 grid((T + kLT - 1) / kLT, (E + kLE - 1) / kLE);
         if (a.x_bf16)

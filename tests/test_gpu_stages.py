@@ -31,7 +31,7 @@ def lcfg(wl):
     ("tiny_fp32", 1), ("tiny_fp32", 4), ("tiny_fp32", 33),
     ("decode_t8", 1), ("decode_t8", 8), ("decode_t8", 16), ("decode_t8", 17),
     ("skew_t64", 64), ("decode_t8", 300), ("prefill_t2048", 2048), ("decode_t8", 100),
-    ("prefill_fp8_t16384", 16384), ("decode_t8", 512), ("decode_t8", 700),
+    ("prefill_fp8_t16384", 16384), ("decode_t8", 512), ("decode_t8", 700), ("decode_t8", 1024),
 ])
 def test_route_parity(wname, T):
     say(f"route {wname} T={T}")
