@@ -12,11 +12,11 @@ namespace beam {
 
 constexpr int kPermThreads = 256;
 constexpr int kPermFused = 4096;   // pairs up to which one workgroup does the whole permutation
-// pairs per workgroup in the multi-block path: 1024 up to 32768 pairs (the
-// scatter of a chunk is serial over its 256-pair steps, so smaller chunks
-// spread it over more workgroups), 4096 above (the one-workgroup scan walks
-// every chunk's histogram in turn)
-static int perm_chunk(int TK) { return TK <= 32768 ? 1024 : 4096; }
+// pairs per workgroup in the multi-block path: the scatter of a chunk is
+// serial over its 256-pair steps, so small chunks spread it over many
+// workgroups (128 at 131072 pairs); the scan reads the chunks' histograms
+// eight at a time, so their number costs it little
+constexpr int kPermChunk = 1024;
 constexpr int kMaxE = 256;
 
 // Stable scatter of pairs [begin, end) given per-expert cursors in LDS
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(256) void beam_quantize_x_e4m3(
     quantize_row_e4m3_wave<NIT>(load_raw, widen, H, xq + row * H, xscale + row);
 }
 
-static int n_chunks(int TK) { return TK <= kPermFused ? 1 : (TK + perm_chunk(TK) - 1) / perm_chunk(TK); }
+static int n_chunks(int TK) { return TK <= kPermFused ? 1 : (TK + kPermChunk - 1) / kPermChunk; }
 
 size_t permute_ws_bytes(int T, int K, int E) {
     const int nb = n_chunks(T * K);
@@ -188,7 +188,7 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t st) {
     } else {
         int32_t* bh = static_cast<int32_t*>(a.ws);
         int32_t* bb = bh + (size_t)nb * a.E;
-        const int chunk = perm_chunk(TK);
+        const int chunk = kPermChunk;
         hipLaunchKernelGGL(beam_permute_hist, dim3(nb), dim3(kPermThreads), 0, st, a.ids, a.e_base, TK, a.E,
                            chunk, bh);
         hipLaunchKernelGGL(beam_permute_scan, dim3(1), dim3(kPermThreads), 0, st, bh, nb, TK, a.E,

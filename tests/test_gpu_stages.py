@@ -123,7 +123,7 @@ def _run_permute(ids_np, E, K):
 @pytest.mark.parametrize("T,E,K,skew", [
     (1, 16, 4, 0.0), (37, 16, 4, 3.0), (8, 256, 8, 0.0), (64, 256, 8, 1.1), (511, 256, 8, 0.0),
     (512, 256, 8, 0.0), (513, 256, 8, 2.0), (2048, 256, 8, 0.0), (16384, 256, 8, 0.0),
-    # the multi-block path's chunk size changes above 32768 pairs (1024 -> 4096)
+    # multi-block path: 32 and 33 chunks of 1024 pairs, ragged, skewed
     (4096, 256, 8, 1.5), (4097, 256, 8, 0.0), (1000, 256, 8, 3.0),
 ])
 def test_permute_parity(T, E, K, skew):
