@@ -15,7 +15,7 @@ constexpr int kPermFused = 4096;   // pairs up to which one workgroup does the w
 // pairs per workgroup in the multi-block path: the scatter of a chunk is
 // serial over its 256-pair steps, so small chunks spread it over many
 // workgroups (128 at 131072 pairs); the scan reads the chunks' histograms
-// eight at a time, so their number costs it little
+// 32 at a time, so their number costs it little
 constexpr int kPermChunk = 1024;
 constexpr int kMaxE = 256;
 
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kPermThreads) void beam_permute_scan(
     const int e = threadIdx.x;
     // the chunks' counts of expert e, kScanBatch loads in flight at a time
     // (indices past the last chunk re-read it and count zero)
-    constexpr int kScanBatch = 8;
+    constexpr int kScanBatch = 32;
     const int ec = e < E ? e : 0;
     auto load_batch = [&](int b0, int (&v)[kScanBatch]) {
 #pragma unroll
